@@ -1,0 +1,270 @@
+"""Pins of the float64 oracle: checks against facts fixed outside the oracle itself.
+
+Each ``check_*`` takes the oracle module (so a deliberately broken copy can be passed
+in by the mutation tests) and raises AssertionError when a pin fails.  Sources of
+truth: closed forms, library routines (torch CPU float64 scaled_dot_product_attention,
+torch's bf16 / float8_e4m3fn conversions), brute force on tiny inputs, invariants.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+
+
+def _sdpa_causal_row(q, k, v, t, sm):
+    """Library reference: torch SDPA (float64, CPU) with an explicit causal mask row."""
+    H, d = q.shape
+    qt = torch.from_numpy(q).reshape(1, H, 1, d)
+    kt = torch.from_numpy(np.ascontiguousarray(k)).reshape(1, 1, -1, d).expand(1, H, -1, d)
+    vt = torch.from_numpy(np.ascontiguousarray(v)).reshape(1, 1, -1, d).expand(1, H, -1, d)
+    mask = torch.zeros(1, 1, 1, k.shape[0], dtype=torch.bool)
+    mask[..., : t + 1] = True
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=sm)
+    return o.reshape(H, d).numpy()
+
+
+def check_dense_vs_sdpa(O, seed=0):
+    rng = np.random.default_rng(seed)
+    for (H, d, N, t) in [(4, 16, 37, 36), (4, 16, 37, 0), (3, 8, 50, 21), (16, 64, 300, 299)]:
+        q = rng.standard_normal((H, d))
+        k = rng.standard_normal((N, d)) * 1.3
+        v = rng.standard_normal((N, d))
+        sm = 1.0 / math.sqrt(d)
+        o, p = O.dense_attention(q, k, v, t, sm)
+        ref = _sdpa_causal_row(q, k, v, t, sm)
+        assert p.shape == (H, t + 1)
+        assert np.max(np.abs(o - ref)) <= 1e-12, "dense attention differs from SDPA"
+
+
+def check_identical_keys(O):
+    """Identical keys: uniform p = 1/(t+1), O = mean of visible V rows, score = H/(t+1),
+    ties resolve to the lowest indices."""
+    rng = np.random.default_rng(1)
+    H, d, N, t, W, kg = 5, 8, 400, 330, 16, 100
+    q = rng.standard_normal((H, d))
+    k = np.tile(rng.standard_normal((1, d)), (N, 1))
+    v = rng.standard_normal((N, d))
+    o, p = O.dense_attention(q, k, v, t, 1.0 / math.sqrt(d))
+    assert np.allclose(p, 1.0 / (t + 1), rtol=0, atol=1e-15)
+    assert np.allclose(o, v[: t + 1].mean(axis=0)[None, :], rtol=0, atol=1e-13)
+    sc = O.selection_scores(p, t, W)
+    assert sc.shape == (t - W + 1,)
+    assert np.allclose(sc, H / (t + 1), rtol=0, atol=1e-14)
+    g = O.select_global(np.full(sc.shape, H / (t + 1)), kg)
+    assert np.array_equal(g, np.arange(kg))
+
+
+def check_score_mass(O):
+    """Each head's probabilities sum to one, so candidate scores plus the window's
+    mass over all heads equals H."""
+    rng = np.random.default_rng(2)
+    H, d, N, W = 6, 16, 260, 32
+    q = rng.standard_normal((H, d)) * 2
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    for t in (259, 100, W - 1, W, 5):
+        _, p = O.dense_attention(q, k, v, t, 0.25)
+        sc = O.selection_scores(p, t, W)
+        C = max(0, t - W + 1)
+        assert sc.shape == (C,)
+        win_mass = p[:, C: t + 1].sum()
+        assert abs(sc.sum() + win_mass - H) <= 1e-12
+        # window mass is exactly the probability of the last min(W, t+1) positions
+        assert abs(win_mass - p[:, max(0, t - W + 1):].sum()) <= 1e-12
+
+
+def check_onehot_keys(O):
+    """Orthogonal one-hot keys: q = e_a gives logit sm*c on key a and 0 elsewhere."""
+    H, d, t, c = 2, 8, 7, 3.0
+    k = np.zeros((t + 1, d))
+    for j in range(t + 1):
+        k[j, j] = c
+    q = np.zeros((H, d))
+    q[0, 2] = 1.0
+    q[1, 5] = 1.0
+    v = np.arange((t + 1) * d, dtype=np.float64).reshape(t + 1, d)
+    sm = 0.5
+    _, p = O.dense_attention(q, k, v, t, sm)
+    z = math.exp(sm * c) + t
+    for h, a in ((0, 2), (1, 5)):
+        assert abs(p[h, a] - math.exp(sm * c) / z) <= 1e-15
+        others = np.delete(p[h], a)
+        assert np.allclose(others, 1.0 / z, rtol=0, atol=1e-15)
+
+
+def _rank_count_select(scores, k):
+    """Brute force from the definition: j is picked iff fewer than k candidates beat it,
+    where i beats j when s_i > s_j, or s_i == s_j and i < j."""
+    n = len(scores)
+    sel = []
+    for j in range(n):
+        beat = sum(1 for i in range(n) if scores[i] > scores[j] or (scores[i] == scores[j] and i < j))
+        if beat < k:
+            sel.append(j)
+    return np.array(sel, dtype=np.int64)
+
+
+def check_selection_bruteforce(O, trials=300):
+    rng = np.random.default_rng(3)
+    for _ in range(trials):
+        n = int(rng.integers(1, 13))
+        s = rng.integers(0, 4, size=n).astype(np.float64)  # many exact ties
+        for k in range(0, n + 2):
+            got = O.select_global(s, k)
+            exp = _rank_count_select(list(s), k)
+            assert np.array_equal(got, exp), (s, k, got, exp)
+
+
+def check_selection_exhaustive(O):
+    """For n <= 8, among all k-subsets the picked one has the largest score multiset and,
+    among equal multisets, the lexicographically smallest index list."""
+    rng = np.random.default_rng(4)
+    for _ in range(60):
+        n = int(rng.integers(1, 9))
+        s = rng.integers(0, 3, size=n).astype(np.float64)
+        for k in range(1, n + 1):
+            best = None
+            for sub in itertools.combinations(range(n), k):
+                key = (tuple(sorted((-s[i] for i in sub))), sub)
+                if best is None or key < best:
+                    best = key
+            assert tuple(O.select_global(s, k)) == best[1]
+
+
+def check_window_enumeration(O, k=1024, W=128, t_max=1300):
+    """Exact index lists for every position 0..t_max on identical scores."""
+    for t in range(t_max + 1):
+        C = max(0, t - W + 1)
+        exp = [-1] * (k + W)
+        for j in range(min(k, C)):
+            exp[j] = j                               # identical scores: lowest indices
+        w = [j for j in range(t - W + 1, t + 1) if j >= 0]
+        for i, j in enumerate(w):
+            exp[k + i] = j
+        g = O.select_global(np.ones(C), k)
+        got = O.assemble_indices(g, t, k, W)
+        assert got.dtype == np.int32 and got.shape == (k + W,)
+        assert got.tolist() == exp, t
+
+
+def check_sparse_identity(O):
+    """If the selection keeps every visible position, sparse attention is dense causal
+    attention of the same query (library routine)."""
+    rng = np.random.default_rng(5)
+    H, d, N, W, kg = 4, 16, 90, 8, 100
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    sm = 1.0 / math.sqrt(d)
+    for t in (89, 50, 3):
+        _, idx, _ = O.full_attn_select_row(q, k, v, t, sm, kg, W)
+        o_sp = O.sparse_attention_row(q, k, v, idx, sm)
+        assert np.max(np.abs(o_sp - _sdpa_causal_row(q, k, v, t, sm))) <= 1e-12
+
+
+def check_sparse_order_invariance(O):
+    rng = np.random.default_rng(6)
+    H, d, N = 4, 16, 200
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    idx = rng.choice(N, size=40, replace=False).astype(np.int32)
+    base = O.sparse_attention_row(q, k, v, idx, 0.3)
+    for _ in range(5):
+        perm = rng.permutation(np.concatenate([idx, -np.ones(9, dtype=np.int32)]))
+        assert np.max(np.abs(O.sparse_attention_row(q, k, v, perm, 0.3) - base)) <= 1e-12
+    # a direct per-head definition: o[h] = sum_j w_j v_j / sum_j w_j, w_j = exp(0.3 q.k_j)
+    for h in range(H):
+        w = np.array([math.exp(0.3 * float(q[h] @ k[j])) for j in idx])
+        ref = (w[:, None] * v[idx]).sum(axis=0) / w.sum()
+        assert np.max(np.abs(base[h] - ref)) <= 1e-12
+
+
+def check_needles(O):
+    """A key planted as 4x a query head wins that head's softmax, is selected, and the
+    head's output is (nearly) that key's value row."""
+    rng = np.random.default_rng(7)
+    H, d, N, W, kg = 8, 64, 3000, 128, 64
+    q = rng.standard_normal((H, d))
+    k = rng.standard_normal((N, d))
+    v = rng.standard_normal((N, d))
+    t, h, p = N - 1, 3, 1234
+    k[p] = 4.0 * q[h]
+    o, idx, score = O.full_attn_select_row(q, k, v, t, 1.0 / math.sqrt(d), kg, W)
+    assert p in set(idx[:kg].tolist())
+    assert score[p] >= 0.99
+    assert np.max(np.abs(o[h] - v[p])) <= 1e-6
+
+
+def check_bf16(O):
+    # all 2^16 patterns against torch's bfloat16 decoding
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    mine = O.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    # encoder: exact ties round to even (closed forms), values beyond a tie round up
+    cases = {1.0 + 2.0 ** -8: 1.0, 1.0 + 3 * 2.0 ** -8: 1.0 + 2.0 ** -6,
+             1.0 + 2.0 ** -8 + 2.0 ** -40: 1.0 + 2.0 ** -7, -(1.0 + 2.0 ** -8): -1.0,
+             3.0: 3.0, 2.0 ** -130: 2.0 ** -130, 0.0: 0.0}
+    xs = np.array(list(cases.keys()))
+    got = O.bf16_bits_to_f64(O.f64_to_bf16_bits_rne(xs))
+    assert np.array_equal(got, np.array(list(cases.values())))
+    # float32-representable inputs: torch's conversion is a single RNE rounding
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    ties = (rng.integers(0, 1 << 16, 4000).astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties[np.isfinite(ties)]])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(O.f64_to_bf16_bits_rne(x.astype(np.float64)), ref)
+
+
+def check_e4m3fn(O):
+    codes = np.arange(256, dtype=np.uint8)
+    mine = O.e4m3fn_bits_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(mine), nan)
+    assert np.array_equal(mine[~nan], ref[~nan])
+    # closed-form points of the format: max normal, min normal, min subnormal, one
+    pts = {0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+           0x38: 1.0, 0xB8: -1.0, 0x00: 0.0}
+    for c, val in pts.items():
+        assert mine[c] == val, (hex(c), mine[c], val)
+    sc = np.array([0.5, 3.0], dtype=np.float32)
+    dec = O.decode(np.array([[0x38, 0x7E], [0x01, 0xB8]], dtype=np.uint8), "fp8", sc)
+    assert np.array_equal(dec, np.array([[0.5, 224.0], [3.0 * 2.0 ** -9, -3.0]]))
+
+
+def check_bridge(O):
+    """Small-integer operands make every float64 sum exact; |sums| <= 256 are exact in bf16,
+    so the result must equal the integer matmul.  Ties in the final rounding go to even."""
+    rng = np.random.default_rng(9)
+    T, D, d = 37, 16, 8
+    h = rng.integers(-2, 3, size=(T, D))
+    wk = rng.integers(-2, 3, size=(D, d))
+    wv = rng.integers(-2, 3, size=(D, d))
+
+    def bits(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    k, v = O.kv_bridge(bits(h), bits(wk), bits(wv), row_block=5)
+    exp_k = [[sum(int(h[r, i]) * int(wk[i, c]) for i in range(D)) for c in range(d)] for r in range(T)]
+    exp_v = [[sum(int(h[r, i]) * int(wv[i, c]) for i in range(D)) for c in range(d)] for r in range(T)]
+    assert np.array_equal(O.bf16_bits_to_f64(k), np.array(exp_k, dtype=np.float64))
+    assert np.array_equal(O.bf16_bits_to_f64(v), np.array(exp_v, dtype=np.float64))
+    # rounding of the sum: [1, 1] . [a, b] with a + b exactly halfway between bf16 values
+    hh = bits(np.array([[1.0, 1.0]]))
+    w = np.array([[1.0, 1.0 + 2.0 ** -7], [2.0 ** -8, 2.0 ** -8]])
+    kk, _ = O.kv_bridge(hh, bits(w), bits(w))
+    assert np.array_equal(O.bf16_bits_to_f64(kk)[0], np.array([1.0, 1.0 + 2.0 ** -6]))
+
+
+ALL_CHECKS = [check_dense_vs_sdpa, check_identical_keys, check_score_mass, check_onehot_keys,
+              check_selection_bruteforce, check_selection_exhaustive, check_window_enumeration,
+              check_sparse_identity, check_sparse_order_invariance, check_needles, check_bf16,
+              check_e4m3fn, check_bridge]

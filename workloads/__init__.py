@@ -1,0 +1,10 @@
+"""Seeded synthetic workloads for the hybrid-block attention hot path.
+
+This package only draws random numbers and stores them in the byte formats the
+library consumes (fp32, bf16 bit patterns, FP8 E4M3FN codes with a per-row fp32
+scale).  It holds none of the method's arithmetic: no attention, no scores, no
+selection, no projection.  Both the float64 oracle (``oracle/``) and the HIP
+path consume the bytes produced here.
+"""
+from .configs import CONFIGS, Config, get_config, small_config  # noqa: F401
+from .gen import Workload, make_workload  # noqa: F401
