@@ -1,0 +1,247 @@
+"""Throughput of the hybrid-block hot path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: the full-attention MQA layer with
+token-level selection (hs2_full_attn_select) followed by the index-reusing sparse layers
+(hs2_sparse_attn), plus the KV bridge for the prefill-exit workload.  Inputs are resident in
+HBM before the timed region.  Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode128k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query tokens/s for select+sparse attn at 128K & 1M ctx; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def upload(wl, dev):
+    import torch
+
+    def up(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    cfg = wl.cfg
+    t = {"q": up(wl.q_full, cfg.q_dtype), "qs": [up(x, cfg.q_dtype) for x in wl.q_sparse],
+         "q_pos": up(wl.q_pos, "i32"), "kv_len": up(wl.kv_len, "i32"), "k_scale": None, "v_scale": None}
+    if cfg.bridge_D:
+        t["hidden"], t["wk"], t["wv"] = up(wl.hidden, "bf16"), up(wl.wk, "bf16"), up(wl.wv, "bf16")
+        t["k"] = torch.empty((1, cfg.N, cfg.d), dtype=torch.bfloat16, device=dev)
+        t["v"] = torch.empty((1, cfg.N, cfg.d), dtype=torch.bfloat16, device=dev)
+    else:
+        t["k"], t["v"] = up(wl.k, cfg.kv_dtype), up(wl.v, cfg.kv_dtype)
+        if cfg.kv_dtype == "fp8":
+            t["k_scale"], t["v_scale"] = up(wl.k_scale, "f32"), up(wl.v_scale, "f32")
+    return t
+
+
+def kv_bytes_per_row(cfg):
+    b = {"bf16": 2, "f32": 4, "fp8": 1}[cfg.kv_dtype]
+    return cfg.d * b + (4 if cfg.kv_dtype == "fp8" else 0)
+
+
+def algorithmic(cfg):
+    """Algorithmic bytes / flops per launch of each kernel, and per step (what the method must
+    move or compute; the second K pass of the score and split bookkeeping are excluded)."""
+    rows = cfg.B * cfg.Tq
+    kvb = kv_bytes_per_row(cfg)
+    qb = {"bf16": 2, "f32": 4}[cfg.q_dtype] * cfg.H * cfg.d
+    # visible (query, key) pairs and unique cache rows touched
+    pairs = sum(cfg.N - cfg.Tq + i + 1 for i in range(cfg.Tq)) * cfg.B
+    full_bytes = cfg.B * cfg.N * 2 * kvb + rows * (qb + cfg.H * cfg.d * 4 + cfg.S * 4)
+    full_flops = 4.0 * cfg.H * cfg.d * pairs
+    sparse_bytes = rows * (cfg.S * 2 * kvb + cfg.S * 4 + qb + cfg.H * cfg.d * 4)
+    sparse_flops = 4.0 * cfg.H * cfg.d * cfg.S * rows
+    out = {
+        "full_attn": {"bytes": cfg.B * cfg.N * 2 * kvb, "flops": full_flops},
+        "sparse_attn": {"bytes": sparse_bytes, "flops": sparse_flops},
+        "step": {"bytes": full_bytes + cfg.n_sparse * sparse_bytes,
+                 "flops": full_flops + cfg.n_sparse * sparse_flops},
+    }
+    if cfg.bridge_D:
+        out["bridge"] = {"bytes": cfg.N * (cfg.bridge_D * 2 + 4 * cfg.d) + 4 * cfg.bridge_D * cfg.d,
+                         "flops": 2.0 * cfg.N * cfg.bridge_D * 2 * cfg.d}
+        out["step"]["bytes"] += out["bridge"]["bytes"]
+        out["step"]["flops"] += out["bridge"]["flops"]
+    return out
+
+
+# kernel name -> (algorithmic unit key, bound)
+KERNEL_UNITS = {
+    "full_attn_generic": ("full_attn", "hbm"),
+    "full_attn_mfma": ("full_attn", "hbm"),
+    "sparse_attn_generic": ("sparse_attn", "hbm"),
+    "sparse_attn_mfma": ("sparse_attn", "hbm"),
+    "bridge_generic": ("bridge", "hbm"),
+    "bridge_mfma": ("bridge", "hbm"),
+}
+
+
+def run_gpu(cfg, steps, warmup, profile=True):
+    import torch
+
+    import token_level_sparse_mqa_amd as hs2
+    from workloads import make_workload
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name}")
+    wl = make_workload(cfg)
+    t = upload(wl, dev)
+    sm = 1.0 / math.sqrt(cfg.d)
+    R = cfg.B * cfg.Tq
+    kvd = hs2.dtype_code(t["k"])
+    ws = torch.empty((hs2.hs2_full_attn_select_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global,
+                                                               cfg.window, kvd),), dtype=torch.uint8, device=dev)
+    sws = torch.empty((hs2.hs2_sparse_attn_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S),),
+                      dtype=torch.uint8, device=dev)
+    o = torch.empty((cfg.B, cfg.Tq, cfg.H, cfg.d), dtype=torch.float32, device=dev)
+    idx = torch.empty((cfg.B, cfg.Tq, cfg.S), dtype=torch.int32, device=dev)
+    o_sp = [torch.empty_like(o) for _ in range(cfg.n_sparse)]
+
+    def step():
+        if cfg.bridge_D:
+            hs2.hs2_kv_bridge(t["hidden"], t["wk"], t["wv"], k_out=t["k"][0], v_out=t["v"][0])
+        hs2.hs2_full_attn_select(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
+                                 v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
+                                 o=o, idx=idx, workspace=ws)
+        for l in range(cfg.n_sparse):
+            hs2.hs2_sparse_attn(t["qs"][l], t["k"], t["v"], idx, kv_len=t["kv_len"], k_scale=t["k_scale"],
+                                v_scale=t["v_scale"], sm_scale=sm, o=o_sp[l], workspace=sws)
+
+    log(f"[bench] warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {steps} steps")
+    hs2.profile_enable(profile)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = e0.elapsed_time(e1) / steps
+    kernels = hs2.profile_read() if profile else {}
+    hs2.profile_enable(False)
+    return {"ms_per_step": ms, "wall_s": wall, "rows": R, "kernels": kernels, "wl": wl}
+
+
+def cpu_baseline(cfg, wl, budget_s=20.0):
+    """The float64 oracle on a bounded sample of the same workload (whole query rows, each with
+    the full layer, selection and every sparse layer)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sm = 1.0 / math.sqrt(cfg.d)
+    t0 = time.perf_counter()
+    done = 0
+    rows = [(b, i) for b in range(cfg.B) for i in range(cfg.Tq)]
+    decoded = {}
+    for (b, i) in rows:
+        if b not in decoded:
+            if cfg.bridge_D:
+                kb, vb = oracle.kv_bridge(wl.hidden, wl.wk, wl.wv)
+                decoded[b] = (oracle.decode(kb, "bf16"), oracle.decode(vb, "bf16"))
+            else:
+                ks = wl.k_scale[b] if wl.k_scale is not None else None
+                vs = wl.v_scale[b] if wl.v_scale is not None else None
+                decoded[b] = (oracle.decode(wl.k[b], cfg.kv_dtype, ks), oracle.decode(wl.v[b], cfg.kv_dtype, vs))
+        k, v = decoded[b]
+        q = oracle.decode(wl.q_full[b, i], cfg.q_dtype)
+        t = int(wl.q_pos[b, i])
+        _, idx, _ = oracle.full_attn_select_row(q, k, v, t, sm, cfg.k_global, cfg.window)
+        for l in range(cfg.n_sparse):
+            oracle.sparse_attention_row(oracle.decode(wl.q_sparse[l][b, i], cfg.q_dtype), k, v, idx, sm)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} of {len(rows)} query rows of {cfg.name} (full layer + selection + "
+                      f"{cfg.n_sparse} sparse layers each, incl. decoding the cache), {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode128k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: the hot path is measured on one GPU's share "
+              f"(sharding is described in DESIGN.md); got --gpus {args.gpus}, WORLD_SIZE {world}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    from workloads import CONFIGS
+    cfg = CONFIGS[args.workload]
+    res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
+    ms = res["ms_per_step"]
+    value = res["rows"] / (ms / 1e3)
+    alg = algorithmic(cfg)
+
+    kernels = {}
+    for name, (tot, n) in res["kernels"].items():
+        kernels[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    roof = None
+    cand = [(v["avg_us"] * v["launches"], k) for k, v in kernels.items() if k in KERNEL_UNITS]
+    if cand:
+        _, kname = max(cand)
+        unit, bound = KERNEL_UNITS[kname]
+        avg_s = kernels[kname]["avg_us"] / 1e6
+        if bound == "hbm":
+            ach = alg[unit]["bytes"] / avg_s / 1e9
+            roof = {"bound": "hbm", "kernel": kname, "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": ach / HBM_PEAK_GBS, "traffic": None}
+        else:
+            ach = alg[unit]["flops"] / avg_s / 1e12
+            roof = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": None}
+    step_frac = {"hbm": alg["step"]["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                 "mfma": alg["step"]["flops"] / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS}
+    out = {
+        "metric": METRIC, "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16"}[cfg.q_dtype] +
+        ("+fp8kv" if cfg.kv_dtype == "fp8" else ""), "data": "synthetic",
+        "config": {"workload": cfg.name, "B": cfg.B, "context": cfg.N, "Tq": cfg.Tq, "H": cfg.H, "d": cfg.d,
+                   "kv_dtype": cfg.kv_dtype, "k_global": cfg.k_global, "window": cfg.window,
+                   "sparse_layers": cfg.n_sparse, "bridge_D": cfg.bridge_D},
+        "roofline": roof, "step_roofline_frac": step_frac, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(cfg, res["wl"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

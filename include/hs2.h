@@ -1,0 +1,167 @@
+/*
+ * hs2.h -- C ABI of the HySparse2 hybrid-block attention hot path on MI355X (gfx950).
+ *
+ * Three operations, in the order a hybrid block runs them:
+ *
+ *   hs2_kv_bridge         KV Bridging: a cross-decoder full-attention layer builds its K/V cache
+ *                         by projecting self-decoder hidden states with its own K and V
+ *                         projections (lynxflow blog, "Two-Level KV Sharing"; agentik-os article,
+ *                         section 2 "Two levels of KV sharing"; ainews page, mechanism paragraph).
+ *   hs2_full_attn_select  The full-attention MQA layer (one shared KV head: ainews page,
+ *                         experimental-setup paragraph) that, on completion, picks per query token
+ *                         the 1,024 best-scoring earlier positions one by one plus a forced window
+ *                         of the 128 most recent positions (kucoin news flash; lynxflow blog,
+ *                         "Token-Level Sparse Selection"; agentik-os article, section 3).
+ *   hs2_sparse_attn       A sparse layer of the same hybrid block: it reuses the full layer's KV
+ *                         cache and selection indices (KV Reuse: lynxflow "Two-Level KV Sharing";
+ *                         agentik-os section 2) and attends over only the selected rows.
+ *
+ * The pages leave the selection score open (agentik-os, "What is not documented").  This
+ * library uses: score(j) = sum over heads h of the full layer's softmax probability p_h(t, j),
+ * the softmax running over every visible key 0..t (window included); ties go to the lower j.
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer argument except the stream is a DEVICE pointer unless stated otherwise.
+ *    The caller owns all buffers; the library allocates no memory that outlives a call and
+ *    never frees caller memory.  hs2_full_attn_select needs scratch memory, which the caller
+ *    passes as `workspace` (size from hs2_full_attn_select_workspace_size).
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and performs no host/device
+ *    synchronisation.  Calls that share a workspace must be ordered on one stream.
+ *  - Arguments are validated on the host before any HIP call.  On a non-OK status nothing has
+ *    been enqueued and no output was written; hs2_last_error() gives a message.  A failure of
+ *    the HIP runtime at launch returns HS2_ERR_HIP.  Faults inside kernels surface at the
+ *    caller's next synchronisation.
+ *  - Values in device memory (positions, lengths, indices) are not validated on the host.
+ *    Kernels never read outside [0, Nmax) rows for them: a query whose position is outside
+ *    [0, min(kv_len, Nmax)) produces o = 0 and an all -1 index row; index entries outside
+ *    [0, min(kv_len, Nmax)) are skipped like -1.
+ *  - Layouts are dense and row-major in the order the dimensions are listed.
+ *    q: [B, Tq, H, d]; k, v: [B, Nmax, d] (one KV head); k_scale, v_scale: [B, Nmax] fp32;
+ *    q_pos: [B, Tq] int32 absolute positions; kv_len: [B] int32 valid cache rows;
+ *    o: [B, Tq, H, d] fp32; idx: [B, Tq, k_global + window] int32.
+ *  - Supported: d in {64, 128}; 1 <= H <= 32; (q, kv) dtypes (F32, F32), (BF16, BF16) and
+ *    (BF16, FP8_E4M3).  Other combinations return HS2_ERR_UNSUPPORTED.
+ *  - BF16 paths multiply the attention weights and V in fp16 with fp32 accumulation; V values
+ *    must lie within the fp16 range (|v| < 65504).  fp32 paths compute in fp32 throughout.
+ */
+#ifndef HS2_H
+#define HS2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    HS2_OK = 0,
+    HS2_ERR_INVALID_ARG = -1,   /* null pointer, non-positive or inconsistent size */
+    HS2_ERR_UNSUPPORTED = -2,   /* valid but outside the supported set (dtype, d, H) */
+    HS2_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+    HS2_ERR_HIP = -4            /* the HIP runtime reported an error */
+} hs2_status;
+
+typedef enum {
+    HS2_F32 = 0,                /* IEEE binary32 */
+    HS2_BF16 = 1,               /* bfloat16 */
+    HS2_FP8_E4M3 = 2            /* OCP FP8 E4M3FN codes (max 448, no infinities) with a per-row
+                                   fp32 scale: value = decode(code) * scale[row]
+                                   (FP8 caches: ainews page, experimental-setup paragraph) */
+} hs2_dtype;
+
+/*
+ * KV Bridging for one target layer (lynxflow "Two-Level KV Sharing": each target layer keeps its
+ * own K/V projections; ainews mechanism paragraph).
+ *   K[t, c] = bf16_rne( sum_i hidden[t, i] * w_k[i, c] ),  V likewise with w_v,
+ * products and sums in fp32 (MFMA), one rounding to bf16 (nearest, ties to even) at the end.
+ *   hidden : bf16 [T, D] row-major            w_k, w_v : bf16 [D, d] row-major
+ *   k_out, v_out : bf16, row t at element offset t * out_row_stride (out_row_stride >= d), so
+ *                  the rows can be written straight into a larger cache.
+ * Requirements: T >= 0, D >= 1 and D % 64 == 0, d in {64, 128}.  T == 0 is a no-op.
+ */
+hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D,
+                         const void* w_k, const void* w_v, int32_t d,
+                         void* k_out, void* v_out, int64_t out_row_stride,
+                         hipStream_t stream);
+
+/*
+ * Bytes of workspace hs2_full_attn_select needs for these sizes (0 on invalid sizes).
+ * The same value is valid for every call with sizes no larger than these and the same dtype.
+ */
+size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d,
+                                           int64_t Nmax, int32_t k_global, int32_t window,
+                                           hs2_dtype kv_dtype);
+
+/*
+ * Full-attention MQA layer with token-level selection.
+ * For query (b, i) at position t = q_pos[b, i], visible keys j = 0..t:
+ *   s_h(j) = sm_scale * q_h . k_j,  p_h(j) = softmax_j s_h(j),  o[b,i,h] = sum_j p_h(j) v_j
+ *   score(j) = sum_h p_h(j) for the candidates j = 0..t-window (none when t < window)
+ *   idx[b,i, 0:k_global]  = the min(k_global, #candidates) best candidates by (score desc,
+ *                           j asc), in ascending order, then -1 padding;
+ *   idx[b,i, k_global:k_global+window] = max(0, t-window+1) .. t ascending, then -1 padding.
+ * scores_dbg (optional, NULL = off): fp32 [B, Tq, Nmax]; entry j holds score(j) for
+ *   candidates and -1.0f elsewhere.
+ * Requirements: 1 <= k_global <= 4096, 0 <= window <= 4096, sm_scale finite and > 0,
+ *   workspace_bytes >= hs2_full_attn_select_workspace_size(...).  k_scale/v_scale are
+ *   required for HS2_FP8_E4M3 and must be NULL otherwise.  B == 0 or Tq == 0 is a no-op.
+ */
+hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype,
+                                const void* k, const void* v, hs2_dtype kv_dtype,
+                                const float* k_scale, const float* v_scale,
+                                const int32_t* q_pos, const int32_t* kv_len,
+                                int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                int32_t k_global, int32_t window, float sm_scale,
+                                float* o, int32_t* idx, float* scores_dbg,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Sparse (index-reusing) attention layer (KV Reuse).
+ *   o[b,i,h] = sum_{j in sel} softmax_j(sm_scale * q_h . k_j) v_j,
+ *   sel = { idx[b,i,e] : 0 <= e < S, 0 <= idx[b,i,e] < min(kv_len[b], Nmax) }.
+ * The order of idx entries does not matter; -1 entries are skipped; entries must be unique
+ * (a repeated entry is counted once per occurrence).  A row with no valid entry gets o = 0.
+ * kv_len may be NULL (then every row < Nmax is valid).  Same dtype rules as above.
+ * workspace (optional, may be NULL): scratch of hs2_sparse_attn_workspace_size bytes.
+ * Requirements: 1 <= S <= 8192.  B == 0 or Tq == 0 is a no-op.
+ */
+hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype,
+                           const void* k, const void* v, hs2_dtype kv_dtype,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* idx, int32_t S, const int32_t* kv_len,
+                           int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                           float sm_scale, float* o,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of optional workspace that let hs2_sparse_attn split each row's index list over
+ * several workgroups (used when there are few rows, e.g. decode).  With a NULL or smaller
+ * workspace each row is handled by one workgroup; results are the same up to fp32 rounding.
+ */
+size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S);
+
+/* Thread-local message describing the last non-OK status returned on this thread. */
+const char* hs2_last_error(void);
+
+/* Library version string. */
+const char* hs2_version(void);
+
+/*
+ * Per-kernel timing for measurement.  While enabled, every kernel the library launches is
+ * bracketed by HIP events recorded on the caller's stream; hs2_profile_read accumulates the
+ * elapsed time of each kernel name (it synchronises on the recorded events).  Disabled by
+ * default; enabling it adds two event records per launch.  Not thread-safe.
+ *   hs2_profile_enable(1) clears earlier records.
+ *   hs2_profile_read(i, ...) fills the i-th kernel name's totals; returns 0, or -1 past the end.
+ */
+void hs2_profile_enable(int enable);
+int  hs2_profile_read(int i, const char** name, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H */

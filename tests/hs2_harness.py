@@ -1,0 +1,146 @@
+"""Test helpers: upload a workload, run the HIP path through the C ABI, run the oracle on
+the same bytes, and compare with the parity protocol.
+
+Protocol per query row:
+  * window segment of idx: exact;
+  * global segment: min(k, C) unique candidates in [0, C), ascending, then -1 padding;
+    the symmetric difference with the oracle's set only holds candidates whose oracle score
+    is within 1e-6 (absolute) of the oracle's k-th score;
+  * planted needles: always picked;
+  * o of the full layer: max-abs error <= 2e-3 (fp32 / bf16 inputs) or 2e-2 (FP8 KV);
+  * sparse layers: the oracle's indices are fed to the HIP path, outputs within the same bars.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Tuple
+
+import numpy as np
+import torch
+
+import oracle
+from workloads import Workload
+
+BAND = 1e-6
+
+
+def tol_for(kv_dtype: str) -> float:
+    return 2e-2 if kv_dtype == "fp8" else 2e-3
+
+
+def to_dev(arr: np.ndarray, dtype: str, dev="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    if dtype == "fp8":
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+    if dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+    if dtype == "i32":
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.int32)).to(dev)
+    raise ValueError(dtype)
+
+
+def bits_from_dev(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+class GpuRun:
+    """Device copies of a workload and the HIP path's outputs."""
+
+    def __init__(self, wl: Workload, dev="cuda"):
+        import token_level_sparse_mqa_amd as hs2
+        self.hs2 = hs2
+        self.wl = wl
+        cfg = wl.cfg
+        self.cfg = cfg
+        self.q = to_dev(wl.q_full, cfg.q_dtype, dev)
+        self.qs = [to_dev(x, cfg.q_dtype, dev) for x in wl.q_sparse]
+        self.q_pos = to_dev(wl.q_pos, "i32", dev)
+        self.kv_len = to_dev(wl.kv_len, "i32", dev)
+        self.k_scale = self.v_scale = None
+        if cfg.bridge_D:
+            self.hidden = to_dev(wl.hidden, "bf16", dev)
+            self.wk = to_dev(wl.wk, "bf16", dev)
+            self.wv = to_dev(wl.wv, "bf16", dev)
+            self.k = torch.empty((1, cfg.N, cfg.d), dtype=torch.bfloat16, device=dev)
+            self.v = torch.empty((1, cfg.N, cfg.d), dtype=torch.bfloat16, device=dev)
+        else:
+            self.k = to_dev(wl.k, cfg.kv_dtype, dev)
+            self.v = to_dev(wl.v, cfg.kv_dtype, dev)
+            if cfg.kv_dtype == "fp8":
+                self.k_scale = to_dev(wl.k_scale, "f32", dev)
+                self.v_scale = to_dev(wl.v_scale, "f32", dev)
+        self.sm = 1.0 / math.sqrt(cfg.d)
+
+    def bridge(self):
+        self.hs2.hs2_kv_bridge(self.hidden, self.wk, self.wv, k_out=self.k[0], v_out=self.v[0])
+
+    def full(self, scores_dbg=False):
+        cfg = self.cfg
+        dbg = None
+        if scores_dbg:
+            dbg = torch.empty((cfg.B, cfg.Tq, cfg.N), dtype=torch.float32, device=self.q.device)
+        o, idx = self.hs2.hs2_full_attn_select(self.q, self.k, self.v, self.q_pos, self.kv_len,
+                                               k_scale=self.k_scale, v_scale=self.v_scale,
+                                               k_global=cfg.k_global, window=cfg.window, sm_scale=self.sm,
+                                               scores_dbg=dbg)
+        return o, idx, dbg
+
+    def sparse(self, layer: int, idx: torch.Tensor, workspace=True):
+        cfg = self.cfg
+        ws = None
+        if workspace:
+            n = self.hs2.hs2_sparse_attn_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, idx.shape[-1])
+            ws = torch.empty((n,), dtype=torch.uint8, device=self.q.device)
+        return self.hs2.hs2_sparse_attn(self.qs[layer], self.k, self.v, idx, kv_len=self.kv_len,
+                                        k_scale=self.k_scale, v_scale=self.v_scale, sm_scale=self.sm,
+                                        workspace=ws)
+
+
+class OracleRun:
+    """The oracle on the same bytes (float64 decode).  Bridge configs use the oracle's own bridge."""
+
+    def __init__(self, wl: Workload):
+        cfg = wl.cfg
+        self.cfg, self.wl = cfg, wl
+        self.q = oracle.decode(wl.q_full, cfg.q_dtype)
+        self.qs = [oracle.decode(x, cfg.q_dtype) for x in wl.q_sparse]
+        if cfg.bridge_D:
+            kb, vb = oracle.kv_bridge(wl.hidden, wl.wk, wl.wv)
+            self.k_bits, self.v_bits = kb, vb
+            self.k = oracle.decode(kb, "bf16")[None]
+            self.v = oracle.decode(vb, "bf16")[None]
+        else:
+            self.k = oracle.decode(wl.k, cfg.kv_dtype, wl.k_scale)
+            self.v = oracle.decode(wl.v, cfg.kv_dtype, wl.v_scale)
+        self.sm = 1.0 / math.sqrt(cfg.d)
+
+    def full_row(self, b: int, i: int):
+        t = int(self.wl.q_pos[b, i])
+        return oracle.full_attn_select_row(self.q[b, i], self.k[b], self.v[b], t, self.sm,
+                                           self.cfg.k_global, self.cfg.window)
+
+    def sparse_row(self, layer: int, b: int, i: int, idx_row: np.ndarray):
+        return oracle.sparse_attention_row(self.qs[layer][b, i], self.k[b], self.v[b], idx_row, self.sm)
+
+
+def check_indices(idx_gpu: np.ndarray, idx_o: np.ndarray, score_o: np.ndarray, t: int, k: int, W: int,
+                  needles: List[int] = ()) -> dict:
+    """Parity protocol for one row; raises AssertionError on violation.  Returns stats."""
+    assert np.array_equal(idx_gpu[k:], idx_o[k:]), f"window segment differs at t={t}"
+    C = score_o.shape[0]
+    n = min(k, C)
+    g = idx_gpu[:k]
+    assert np.all(g[n:] == -1), "global padding"
+    gs = g[:n]
+    assert np.all(gs >= 0) and np.all(gs < C), "global pick outside the candidates"
+    assert np.all(np.diff(gs) > 0), "global picks not strictly ascending"
+    go = idx_o[:n]
+    diff = np.setxor1d(gs, go)
+    kth = np.sort(score_o)[::-1][n - 1] if n > 0 else 0.0
+    if diff.size:
+        off = np.abs(score_o[diff] - kth)
+        assert np.all(off <= BAND), f"selection differs outside the band: max |score-kth| = {off.max():.3e}"
+    for p in needles:
+        assert p in set(gs.tolist()), f"needle {p} not picked"
+    return {"mismatch": int(diff.size // 2), "n": n}

@@ -1,0 +1,112 @@
+"""CPU: the C-ABI library loads, exports every function include/hs2.h declares, and rejects
+bad arguments on the host before any HIP call (no GPU needed: nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import token_level_sparse_mqa_amd as hs2
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000        # never dereferenced: validation fails before any launch
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "hs2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = hs2.lib()
+    names = _declared()
+    assert {"hs2_kv_bridge", "hs2_full_attn_select", "hs2_sparse_attn",
+            "hs2_full_attn_select_workspace_size", "hs2_last_error", "hs2_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+    assert "gfx950" in hs2.hs2_version()
+
+
+def _fas(**kw):
+    a = dict(q=FAKE, qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, qp=FAKE, kl=FAKE,
+             B=1, Tq=1, H=32, d=128, N=4096, kg=1024, W=128, sm=0.088, o=FAKE, idx=FAKE, dbg=None,
+             ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return hs2.lib().hs2_full_attn_select(a["q"], a["qd"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"], a["qp"],
+                                          a["kl"], a["B"], a["Tq"], a["H"], a["d"], a["N"], a["kg"], a["W"],
+                                          a["sm"], a["o"], a["idx"], a["dbg"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(H=33), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(H=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(qd=hs2.HS2_F32), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(kvd=hs2.HS2_FP8_E4M3), hs2.HS2_ERR_INVALID_ARG),            # scales missing
+    (dict(ks=FAKE, vs=FAKE), hs2.HS2_ERR_INVALID_ARG),               # scales on a bf16 cache
+    (dict(kg=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(kg=5000), hs2.HS2_ERR_INVALID_ARG),
+    (dict(W=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(sm=0.0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(sm=float("inf")), hs2.HS2_ERR_INVALID_ARG),
+    (dict(q=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(idx=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(qp=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
+    (dict(wsb=1024), hs2.HS2_ERR_WORKSPACE),
+    (dict(B=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(N=0), hs2.HS2_ERR_INVALID_ARG),
+])
+def test_full_attn_select_rejects(kw, status):
+    assert _fas(**kw) == status
+    assert hs2.hs2_last_error()
+
+
+def test_empty_batch_returns_ok_without_launch():
+    assert _fas(B=0, q=None, k=None, v=None, o=None, idx=None, ws=None) == hs2.HS2_OK
+    assert _fas(Tq=0) == hs2.HS2_OK
+
+
+def test_workspace_size():
+    n = hs2.hs2_full_attn_select_workspace_size(8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16)
+    # at least the fp32 score rows of every query
+    assert n >= 8 * 131072 * 4
+    assert hs2.hs2_full_attn_select_workspace_size(1, 1, 32, 96, 100, 1024, 128, hs2.HS2_BF16) == 0
+    assert hs2.hs2_full_attn_select_workspace_size(1, 1, 32, 128, 100, 0, 128, hs2.HS2_BF16) == 0
+    # monotone in the sizes it is given
+    a = hs2.hs2_full_attn_select_workspace_size(1, 16, 16, 64, 4096, 1024, 128, hs2.HS2_F32)
+    b = hs2.hs2_full_attn_select_workspace_size(1, 16, 16, 64, 8192, 1024, 128, hs2.HS2_F32)
+    assert 0 < a < b
+
+
+def _sp(**kw):
+    a = dict(q=FAKE, qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, idx=FAKE, S=1152,
+             kl=None, B=1, Tq=1, H=32, d=128, N=4096, sm=0.088, o=FAKE, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return hs2.lib().hs2_sparse_attn(a["q"], a["qd"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"], a["idx"],
+                                     a["S"], a["kl"], a["B"], a["Tq"], a["H"], a["d"], a["N"], a["sm"], a["o"],
+                                     a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(S=9000), hs2.HS2_ERR_INVALID_ARG),
+    (dict(idx=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(d=32), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(kvd=hs2.HS2_F32), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(o=None), hs2.HS2_ERR_INVALID_ARG),
+])
+def test_sparse_rejects(kw, status):
+    assert _sp(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 10, 100, FAKE, FAKE, 128, FAKE, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),   # D % 64
+    ((FAKE, 10, 128, FAKE, FAKE, 96, FAKE, FAKE, 128, None), hs2.HS2_ERR_UNSUPPORTED),
+    ((FAKE, 10, 128, FAKE, FAKE, 128, FAKE, FAKE, 64, None), hs2.HS2_ERR_INVALID_ARG),    # stride < d
+    ((None, 10, 128, FAKE, FAKE, 128, FAKE, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),
+    ((None, 0, 128, None, None, 128, None, None, 128, None), hs2.HS2_OK),                 # T == 0
+])
+def test_bridge_rejects(args, status):
+    assert hs2.lib().hs2_kv_bridge(*args) == status

@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle on the same bytes.
+
+Small cases span several key tiles, ragged tails and the method's degenerate cases; the five
+workloads run at full size with every row (decode) or sampled rows (prefill chunks) checked.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from tests.hs2_harness import GpuRun, OracleRun, check_indices, tol_for, to_dev, bits_from_dev
+from workloads import CONFIGS, make_workload, small_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=1e-7):
+    _say(f"[parity] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} H={cfg.H} d={cfg.d} "
+         f"{cfg.q_dtype}/{cfg.kv_dtype} k={cfg.k_global} W={cfg.window}")
+    wl = make_workload(cfg)
+    g = GpuRun(wl)
+    if cfg.bridge_D:
+        g.bridge()
+    o, idx, dbg = g.full(scores_dbg=check_scores)
+    torch.cuda.synchronize()
+    o_h, idx_h = o.cpu().numpy(), idx.cpu().numpy()
+    dbg_h = dbg.cpu().numpy() if dbg is not None else None
+    O = OracleRun(wl)
+    if rows is None:
+        rows = [(b, i) for b in range(cfg.B) for i in range(cfg.Tq)]
+    t0 = cfg.N - cfg.Tq
+    needles = {}
+    for (b, t, h, p) in wl.needles:
+        needles.setdefault((b, t - t0), []).append(p)
+    tol = tol_for(cfg.kv_dtype)
+    idx_oracle = idx_h.copy()         # rows not sampled keep the HIP path's own indices
+    stats = {"mismatch": 0, "o_err": 0.0, "score_err": 0.0}
+    for (b, i) in rows:
+        o_o, idx_o, sc_o = O.full_row(b, i)
+        t = int(wl.q_pos[b, i])
+        st = check_indices(idx_h[b, i], idx_o, sc_o, t, cfg.k_global, cfg.window, needles.get((b, i), []))
+        stats["mismatch"] += st["mismatch"]
+        err = float(np.max(np.abs(o_h[b, i] - o_o)))
+        stats["o_err"] = max(stats["o_err"], err)
+        assert err <= tol, f"row {(b, i)}: full-layer o error {err:.3e} > {tol}"
+        if dbg_h is not None:
+            C = sc_o.shape[0]
+            if C:
+                # fp32 logits carry a relative error: bound |d score| by score_tol + 1e-5 * score
+                dsc = np.abs(dbg_h[b, i, :C] - sc_o)
+                serr = float(np.max(dsc))
+                stats["score_err"] = max(stats["score_err"], serr)
+                assert np.all(dsc <= score_tol + 1e-5 * sc_o), f"row {(b, i)}: score error {serr:.3e}"
+            assert np.all(dbg_h[b, i, C:] == -1.0)
+        idx_oracle[b, i] = idx_o
+    idx_dev = to_dev(idx_oracle, "i32")
+    nl = cfg.n_sparse if sparse_layers is None else sparse_layers
+    for layer in range(nl):
+        for ws in (True, False):
+            o_sp = g.sparse(layer, idx_dev, workspace=ws).cpu().numpy()
+            for (b, i) in rows:
+                ref = O.sparse_row(layer, b, i, idx_oracle[b, i])
+                err = float(np.max(np.abs(o_sp[b, i] - ref)))
+                assert err <= tol, f"sparse layer {layer} row {(b, i)} ws={ws}: error {err:.3e} > {tol}"
+    _say(f"[parity] {cfg.name} ok: rows={len(rows)} band-mismatches={stats['mismatch']} "
+         f"o_err={stats['o_err']:.2e} score_err={stats['score_err']:.2e}")
+    return g, wl, idx, O
+
+
+SMALL = [
+    small_config("decode_ragged", 201, B=3, N=5000, Tq=2, n_sparse=2),
+    small_config("fp8_ragged", 202, B=2, N=6001, Tq=1, kv_dtype="fp8", n_sparse=2),
+    small_config("chunk_needles", 203, B=1, N=8192 + 128, Tq=128, n_sparse=1, needles="spread64"),
+    small_config("h16_d64", 204, B=2, N=3000, Tq=3, H=16, d=64, n_sparse=1),
+    small_config("h8_d128", 205, B=1, N=2500, Tq=5, H=8, d=128, n_sparse=1),
+    small_config("f32_h16_d64", 206, B=1, N=4096, Tq=16, H=16, d=64, q_dtype="f32", kv_dtype="f32",
+                 n_sparse=2, needles="seeded8"),
+    small_config("f32_d128", 207, B=2, N=1500, Tq=2, H=32, d=128, q_dtype="f32", kv_dtype="f32", n_sparse=1),
+    # every query before the window end: no candidates, window clamped at 0
+    small_config("short_context", 208, B=1, N=100, Tq=100, n_sparse=1),
+    # around C = k: positions 1148..1155 give C = 1021..1028
+    small_config("k_boundary", 209, B=1, N=1156, Tq=8, n_sparse=1),
+    # fewer candidates than k everywhere
+    small_config("few_candidates", 210, B=2, N=700, Tq=4, n_sparse=1),
+    # identical keys: every score ties; the k-th bucket overflows the LDS list -> exact fallback
+    small_config("all_ties", 211, B=1, N=6000, Tq=2, n_sparse=1, ident_keys=True),
+    small_config("all_ties_small", 212, B=1, N=2000, Tq=2, n_sparse=1, ident_keys=True),
+    # small k and window
+    small_config("k16_w4", 213, B=2, N=777, Tq=3, n_sparse=1, k_global=16, window=4),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=[c.name for c in SMALL])
+def test_small(cfg):
+    run_parity(cfg)
+
+
+def test_deterministic_indices():
+    cfg = SMALL[0]
+    wl = make_workload(cfg)
+    g = GpuRun(wl)
+    _, idx1, _ = g.full()
+    _, idx2, _ = g.full()
+    torch.cuda.synchronize()
+    assert torch.equal(idx1, idx2)
+
+
+def test_empty_batch_is_noop():
+    import token_level_sparse_mqa_amd as hs2
+    q = torch.empty((0, 1, 32, 128), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((0, 16, 128), dtype=torch.bfloat16, device="cuda")
+    qp = torch.empty((0, 1), dtype=torch.int32, device="cuda")
+    kl = torch.empty((0,), dtype=torch.int32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    o, idx = hs2.hs2_full_attn_select(q, k, k, qp, kl, workspace=ws)
+    assert o.shape == (0, 1, 32, 128) and idx.shape == (0, 1, 1152)
+
+
+def test_invalid_positions_give_empty_rows():
+    """A query position outside [0, kv_len) yields o = 0 and an all -1 index row (no fault)."""
+    cfg = small_config("badpos", 214, B=2, N=1500, Tq=2, n_sparse=1)
+    wl = make_workload(cfg)
+    wl.q_pos[0, 0] = 1500       # == kv_len
+    wl.q_pos[1, 1] = -5
+    g = GpuRun(wl)
+    o, idx, _ = g.full()
+    torch.cuda.synchronize()
+    o, idx = o.cpu().numpy(), idx.cpu().numpy()
+    assert np.all(idx[0, 0] == -1) and np.all(idx[1, 1] == -1)
+    assert np.all(o[0, 0] == 0) and np.all(o[1, 1] == 0)
+    assert np.all(idx[0, 1, 1024:] >= 0)
+
+
+def test_bridge_small_exact():
+    """Integer-valued operands: every fp32 partial sum is exact, so the bridge is bit-exact."""
+    import token_level_sparse_mqa_amd as hs2
+    import oracle
+    rng = np.random.default_rng(5)
+    T, D, d = 300, 256, 128
+    h = rng.integers(-3, 4, size=(T, D)).astype(np.float32)
+    wk = rng.integers(-3, 4, size=(D, d)).astype(np.float32)
+    wv = rng.integers(-3, 4, size=(D, d)).astype(np.float32)
+    from workloads.gen import f32_to_bf16_bits
+    hb, wkb, wvb = f32_to_bf16_bits(h), f32_to_bf16_bits(wk), f32_to_bf16_bits(wv)
+    k, v = hs2.hs2_kv_bridge(to_dev(hb, "bf16"), to_dev(wkb, "bf16"), to_dev(wvb, "bf16"))
+    ko, vo = oracle.kv_bridge(hb, wkb, wvb)
+    assert np.array_equal(bits_from_dev(k), ko) and np.array_equal(bits_from_dev(v), vo)
+
+
+def test_bridge_strided_rows():
+    import token_level_sparse_mqa_amd as hs2
+    import oracle
+    from workloads.gen import f32_to_bf16_bits
+    rng = np.random.default_rng(6)
+    T, D, d = 130, 128, 64
+    hb = f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+    wkb = f32_to_bf16_bits((rng.standard_normal((D, d)) * 0.05).astype(np.float32))
+    wvb = f32_to_bf16_bits((rng.standard_normal((D, d)) * 0.05).astype(np.float32))
+    cache = torch.full((T, 3 * d), -7.0, dtype=torch.bfloat16, device="cuda")
+    hs2.hs2_kv_bridge(to_dev(hb, "bf16"), to_dev(wkb, "bf16"), to_dev(wvb, "bf16"),
+                      k_out=cache[:, d:2 * d], v_out=cache[:, 2 * d:], out_row_stride=3 * d)
+    c = bits_from_dev(cache)
+    ko, vo = oracle.kv_bridge(hb, wkb, wvb)
+    assert np.all(oracle.decode(c[:, :d], "bf16") == -7.0)
+    ulp_k = np.abs(c[:, d:2 * d].astype(np.int32) - ko.astype(np.int32))
+    ulp_v = np.abs(c[:, 2 * d:].astype(np.int32) - vo.astype(np.int32))
+    assert ulp_k.max() <= 1 and ulp_v.max() <= 1
+
+
+# ---------------------------------------------------------------------------------------------
+# The five workloads at full size
+# ---------------------------------------------------------------------------------------------
+def test_full_tiny():
+    run_parity(CONFIGS["tiny"])
+
+
+def test_full_decode128k():
+    run_parity(CONFIGS["decode128k"])
+
+
+def test_full_decode1m_fp8():
+    run_parity(CONFIGS["decode1m_fp8"], score_tol=1e-7)
+
+
+def _sample_rows(cfg, wl_needle_rows, n_extra=6, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = {(0, 0), (0, cfg.Tq - 1)}
+    rows.update(wl_needle_rows)
+    rows.update((0, int(i)) for i in rng.choice(cfg.Tq, size=n_extra, replace=False))
+    return sorted(rows)
+
+
+def test_full_prefill_chunk_sampled():
+    cfg = CONFIGS["prefill_chunk"]
+    t0 = cfg.N - cfg.Tq
+    from workloads.gen import _needle_plan
+    plan = _needle_plan(cfg)
+    needle_rows = [(0, plan[i][1] - t0) for i in (0, 17, 40, 63)]
+    run_parity(cfg, rows=_sample_rows(cfg, needle_rows), check_scores=False)
+
+
+def test_full_prefill_exit256k_sampled():
+    cfg = CONFIGS["prefill_exit256k"]
+    g, wl, _, O = run_parity(cfg, rows=_sample_rows(cfg, [], n_extra=4), check_scores=False)
+    # the bridge itself: within one bf16 ulp of the float64 projection, mismatch fraction reported
+    kb, vb = bits_from_dev(g.k[0]), bits_from_dev(g.v[0])
+    ko, vo = O.k_bits, O.v_bits
+    dk = np.abs(kb.astype(np.int32) - ko.astype(np.int32))
+    dv = np.abs(vb.astype(np.int32) - vo.astype(np.int32))
+    _say(f"[parity] bridge mismatch fraction K {np.mean(dk > 0):.2e} V {np.mean(dv > 0):.2e}")
+    assert dk.max() <= 1 and dv.max() <= 1

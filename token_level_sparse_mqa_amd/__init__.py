@@ -1,0 +1,194 @@
+"""Python binding of libhs2 (HySparse2 hybrid-block attention hot path, MI355X / gfx950).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of libhs2.so,
+called through its C ABI (include/hs2.h) with ctypes.  torch provides device memory and
+the current stream.  The functions carry the C names:
+
+    hs2_kv_bridge, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
+    hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_last_error, hs2_version
+
+There is no fallback: if the built library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HS2_F32, HS2_BF16, HS2_FP8_E4M3 = 0, 1, 2
+HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libhs2.so")
+_LIB: Optional[ctypes.CDLL] = None
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "hs2_kv_bridge": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp]),
+    "hs2_full_attn_select_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_int]),
+    "hs2_full_attn_select": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                            _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
+                                            _vp, _vp, _vp, _vp, _sz, _vp]),
+    "hs2_sparse_attn": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _vp,
+                                       _i32, _i32, _i32, _i32, _i64, _f32, _vp, _vp, _sz, _vp]),
+    "hs2_sparse_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "hs2_last_error": (ctypes.c_char_p, []),
+    "hs2_version": (ctypes.c_char_p, []),
+    "hs2_profile_enable": (None, [ctypes.c_int]),
+    "hs2_profile_read": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
+}
+
+
+class HS2Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hs2 status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libhs2.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m token_level_sparse_mqa_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def hs2_last_error() -> str:
+    return lib().hs2_last_error().decode()
+
+
+def hs2_version() -> str:
+    return lib().hs2_version().decode()
+
+
+def _check(status: int):
+    if status != HS2_OK:
+        raise HS2Error(status, hs2_last_error())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return HS2_F32
+    if t.dtype == torch.bfloat16:
+        return HS2_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return HS2_FP8_E4M3
+    raise ValueError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to hs2 must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def hs2_kv_bridge(hidden: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
+                  k_out: Optional[torch.Tensor] = None, v_out: Optional[torch.Tensor] = None,
+                  out_row_stride: Optional[int] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """K = bf16(hidden @ w_k), V = bf16(hidden @ w_v).  hidden [T, D] bf16; w_k, w_v [D, d] bf16."""
+    T, D = hidden.shape
+    d = w_k.shape[1]
+    if k_out is None:
+        k_out = torch.empty((T, d), dtype=torch.bfloat16, device=hidden.device)
+    if v_out is None:
+        v_out = torch.empty((T, d), dtype=torch.bfloat16, device=hidden.device)
+    stride = d if out_row_stride is None else out_row_stride
+    for t in (k_out, v_out):   # rows may sit inside a wider cache: check the row stride instead
+        if t.dim() != 2 or t.shape != (T, d) or t.stride(1) != 1 or (T > 1 and t.stride(0) != stride):
+            raise ValueError("k_out/v_out must be [T, d] views with unit column stride and row stride "
+                             "out_row_stride")
+    _check(lib().hs2_kv_bridge(_ptr(hidden), T, D, _ptr(w_k), _ptr(w_v), d, k_out.data_ptr(),
+                               v_out.data_ptr(), stride, _stream(stream)))
+    return k_out, v_out
+
+
+def hs2_full_attn_select_workspace_size(B: int, Tq: int, H: int, d: int, Nmax: int, k_global: int,
+                                        window: int, kv_dtype: int) -> int:
+    return int(lib().hs2_full_attn_select_workspace_size(B, Tq, H, d, Nmax, k_global, window, kv_dtype))
+
+
+def hs2_sparse_attn_workspace_size(B: int, Tq: int, H: int, d: int, S: int) -> int:
+    return int(lib().hs2_sparse_attn_workspace_size(B, Tq, H, d, S))
+
+
+def hs2_full_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+                         kv_len: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
+                         v_scale: Optional[torch.Tensor] = None, k_global: int = 1024, window: int = 128,
+                         sm_scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                         idx: Optional[torch.Tensor] = None, scores_dbg: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None):
+    """Full-attention MQA layer + token-level selection.  Returns (o fp32 [B,Tq,H,d], idx int32 [B,Tq,k+W])."""
+    B, Tq, H, d = q.shape
+    Nmax = k.shape[1]
+    kvd = dtype_code(k)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Tq, k_global + window), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        n = hs2_full_attn_select_workspace_size(B, Tq, H, d, Nmax, k_global, window, kvd)
+        workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().hs2_full_attn_select(
+        _ptr(q), dtype_code(q), _ptr(k), _ptr(v), kvd, _ptr(k_scale), _ptr(v_scale), _ptr(q_pos), _ptr(kv_len),
+        B, Tq, H, d, Nmax, k_global, window, float(sm_scale), _ptr(o), _ptr(idx), _ptr(scores_dbg),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, idx
+
+
+def hs2_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                    kv_len: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                    v_scale: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                    o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Sparse layer reusing the full layer's KV and indices.  Returns o fp32 [B,Tq,H,d]."""
+    B, Tq, H, d = q.shape
+    Nmax = k.shape[1]
+    S = idx.shape[-1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hs2_sparse_attn(
+        _ptr(q), dtype_code(q), _ptr(k), _ptr(v), dtype_code(k), _ptr(k_scale), _ptr(v_scale), _ptr(idx), S,
+        _ptr(kv_len), B, Tq, H, d, Nmax, float(sm_scale), _ptr(o), _ptr(workspace), wsb, _stream(stream)))
+    return o
+
+
+def profile_enable(enable: bool = True):
+    lib().hs2_profile_enable(1 if enable else 0)
+
+
+def profile_read() -> dict:
+    """{kernel name: (total ms, launches)} accumulated since profile_enable(True)."""
+    out = {}
+    i = 0
+    name = ctypes.c_char_p()
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    while lib().hs2_profile_read(i, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)) == 0:
+        out[name.value.decode()] = (ms.value, n.value)
+        i += 1
+    return out

@@ -1,0 +1,308 @@
+// Host side of the hs2 C ABI: argument validation, workspace planning, kernel dispatch,
+// error reporting and the optional per-kernel timing hook.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "hs2_internal.h"
+
+namespace hs2 {
+namespace {
+
+thread_local std::string g_err;
+
+hs2_status fail(hs2_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+hs2_status hip_fail(hipError_t e, const char* where) {
+    return fail(HS2_ERR_HIP, "%s: HIP error %d (%s)", where, (int)e, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dtype_pair_ok(int qd, int kd) {
+    return (qd == HS2_F32 && kd == HS2_F32) || (qd == HS2_BF16 && kd == HS2_BF16) ||
+           (qd == HS2_BF16 && kd == HS2_FP8_E4M3);
+}
+
+// ---- workspace plan of hs2_full_attn_select ----------------------------------------------------
+struct SelectPlan {
+    int64_t R;
+    int nsplit; int64_t chunk;         // attention pass over keys
+    int score_nsplit; int64_t score_chunk;
+    int nseg;
+    size_t off_part, off_lse, off_scores, off_hist, off_cnt, off_sure, off_cand, total;
+    size_t zero_off, zero_words;       // rowhist + counters, cleared at the start of a call
+};
+
+SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global) {
+    SelectPlan p{};
+    p.R = (int64_t)B * Tq;
+    // enough workgroups to fill 256 CUs several times over, at least 256 keys per split
+    int64_t ns = ceil_div(4096, p.R);
+    const int64_t ns_max = ceil_div(Nmax, 256);
+    if (ns > ns_max) ns = ns_max;
+    if (ns < 1) ns = 1;
+    p.nsplit = (int)ns;
+    p.chunk = ceil_div(ceil_div(Nmax, ns), 32) * 32;
+    p.score_nsplit = p.nsplit;
+    p.score_chunk = p.chunk;
+    p.nseg = (int)ceil_div(Nmax, kSelSeg);
+    size_t off = 0;
+    p.off_part = off;   off = align_up(off + (p.nsplit > 1 ? (size_t)p.R * p.nsplit * H * (d + 2) * 4 : 0));
+    p.off_lse = off;    off = align_up(off + (size_t)p.R * H * 4);
+    p.off_hist = off;   off = off + (size_t)p.R * kHistBins * 4;
+    p.off_cnt = off;    off = align_up(off + (size_t)p.R * 4 * 4);
+    p.zero_off = p.off_hist;
+    p.zero_words = (p.off_cnt + (size_t)p.R * 16 - p.off_hist) / 4;
+    p.off_sure = off;   off = align_up(off + (size_t)p.R * k_global * 4);
+    p.off_cand = off;   off = align_up(off + (size_t)p.R * kSelCap * 8);
+    p.off_scores = off; off = align_up(off + (size_t)p.R * Nmax * 4);
+    p.total = off;
+    return p;
+}
+
+int sparse_nsplit(int64_t R, int S) {
+    int64_t ns = ceil_div(2048, R);
+    const int64_t ns_max = ceil_div(S, 64);
+    if (ns > ns_max) ns = ns_max;
+    return ns < 1 ? 1 : (int)ns;
+}
+
+size_t sparse_ws_bytes(int64_t R, int H, int d, int S) {
+    const int ns = sparse_nsplit(R, S);
+    return ns > 1 ? (size_t)R * ns * H * (d + 2) * 4 : 0;
+}
+
+hs2_status check_common(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                        const float* k_scale, const float* v_scale, int B, int Tq, int H, int d,
+                        int64_t Nmax, float sm_scale, const float* o) {
+    if (B < 0 || Tq < 0) return fail(HS2_ERR_INVALID_ARG, "B and Tq must be >= 0 (got %d, %d)", B, Tq);
+    if (H < 1 || Nmax < 1) return fail(HS2_ERR_INVALID_ARG, "H and Nmax must be >= 1 (got %d, %lld)", H, (long long)Nmax);
+    if (!(sm_scale > 0.f) || !isfinite(sm_scale)) return fail(HS2_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+    if (q_dtype < HS2_F32 || q_dtype > HS2_FP8_E4M3 || kv_dtype < HS2_F32 || kv_dtype > HS2_FP8_E4M3)
+        return fail(HS2_ERR_INVALID_ARG, "unknown dtype (q %d, kv %d)", q_dtype, kv_dtype);
+    if (d != 64 && d != 128) return fail(HS2_ERR_UNSUPPORTED, "head dim d=%d not supported (64 or 128)", d);
+    if (H > 32) return fail(HS2_ERR_UNSUPPORTED, "H=%d query heads not supported (at most 32)", H);
+    if (!dtype_pair_ok(q_dtype, kv_dtype)) return fail(HS2_ERR_UNSUPPORTED, "dtype pair (q %d, kv %d) not supported", q_dtype, kv_dtype);
+    if (kv_dtype == HS2_FP8_E4M3) {
+        if (!k_scale || !v_scale) return fail(HS2_ERR_INVALID_ARG, "FP8 KV needs k_scale and v_scale");
+    } else if (k_scale || v_scale) {
+        return fail(HS2_ERR_INVALID_ARG, "k_scale/v_scale must be NULL unless the KV dtype is FP8");
+    }
+    if ((int64_t)B * Tq > 0 && (!q || !k || !v || !o)) return fail(HS2_ERR_INVALID_ARG, "null q/k/v/o pointer");
+    return HS2_OK;
+}
+
+}  // namespace
+
+// ---- measurement hook ------------------------------------------------------------------------
+namespace {
+struct ProfEntry { std::string name; double ms = 0; int64_t launches = 0; };
+struct ProfPending { int entry; hipEvent_t start, stop; };
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfEntry> g_prof;
+std::vector<ProfPending> g_pending;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t get_event() {
+    if (!g_event_pool.empty()) { hipEvent_t e = g_event_pool.back(); g_event_pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+}  // namespace
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    int entry = -1;
+    for (size_t i = 0; i < g_prof.size(); ++i) if (g_prof[i].name == name) entry = (int)i;
+    if (entry < 0) { g_prof.push_back(ProfEntry{name}); entry = (int)g_prof.size() - 1; }
+    hipEvent_t a = get_event(), b = get_event();
+    if (!a || !b) return;
+    hipEventRecord(a, s);
+    g_pending.push_back(ProfPending{entry, a, b});
+    slot = (int)g_pending.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    hipEventRecord(g_pending[slot].stop, stream);
+}
+
+}  // namespace hs2
+
+using namespace hs2;
+
+extern "C" {
+
+const char* hs2_last_error(void) { return g_err.c_str(); }
+
+const char* hs2_version(void) { return "hs2 0.1.0 (gfx950)"; }
+
+void hs2_profile_enable(int enable) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (enable) {
+        for (auto& p : g_pending) { hipEventSynchronize(p.stop); g_event_pool.push_back(p.start); g_event_pool.push_back(p.stop); }
+        g_pending.clear();
+        g_prof.clear();
+    }
+    g_prof_on = enable != 0;
+}
+
+int hs2_profile_read(int i, const char** name, double* total_ms, int64_t* launches) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& p : g_pending) {
+        float ms = 0.f;
+        hipEventSynchronize(p.stop);
+        if (hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+            g_prof[p.entry].ms += ms;
+            g_prof[p.entry].launches += 1;
+        }
+        g_event_pool.push_back(p.start);
+        g_event_pool.push_back(p.stop);
+    }
+    g_pending.clear();
+    if (i < 0 || i >= (int)g_prof.size()) return -1;
+    if (name) *name = g_prof[i].name.c_str();
+    if (total_ms) *total_ms = g_prof[i].ms;
+    if (launches) *launches = g_prof[i].launches;
+    return 0;
+}
+
+hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D, const void* w_k, const void* w_v, int32_t d,
+                         void* k_out, void* v_out, int64_t out_row_stride, hipStream_t stream) {
+    if (T < 0) return fail(HS2_ERR_INVALID_ARG, "T must be >= 0");
+    if (D < 1 || D % 64 != 0) return fail(HS2_ERR_INVALID_ARG, "D=%d must be a positive multiple of 64", D);
+    if (d != 64 && d != 128) return fail(HS2_ERR_UNSUPPORTED, "d=%d not supported (64 or 128)", d);
+    if (out_row_stride < d) return fail(HS2_ERR_INVALID_ARG, "out_row_stride %lld < d", (long long)out_row_stride);
+    if (T == 0) return HS2_OK;
+    if (!hidden || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARG, "null pointer");
+    BridgeArgs a{(const uint16_t*)hidden, T, D, (const uint16_t*)w_k, (const uint16_t*)w_v, d,
+                 (uint16_t*)k_out, (uint16_t*)v_out, out_row_stride};
+    hipError_t e = launch_bridge_generic(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_bridge launch");
+    return HS2_OK;
+}
+
+size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                           int32_t k_global, int32_t window, hs2_dtype kv_dtype) {
+    (void)kv_dtype; (void)window;
+    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 || k_global < 1 || k_global > 4096)
+        return 0;
+    if ((int64_t)B * Tq == 0) return kAlign;
+    return plan_select(B, Tq, H, d, Nmax, k_global).total;
+}
+
+hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
+                                const float* k_scale, const float* v_scale, const int32_t* q_pos,
+                                const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                int32_t k_global, int32_t window, float sm_scale, float* o, int32_t* idx,
+                                float* scores_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st != HS2_OK) return st;
+    if (k_global < 1 || k_global > 4096) return fail(HS2_ERR_INVALID_ARG, "k_global=%d outside [1, 4096]", k_global);
+    if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
+    if ((int64_t)B * Tq == 0) return HS2_OK;
+    if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global);
+    if (!workspace || workspace_bytes < p.total)
+        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
+
+    char* ws = (char*)workspace;
+    float* lse = (float*)(ws + p.off_lse);
+    float* scores = (float*)(ws + p.off_scores);
+    uint32_t* rowhist = (uint32_t*)(ws + p.off_hist);
+    uint32_t* counters = (uint32_t*)(ws + p.off_cnt);
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
+
+    hipError_t e = launch_zero_u32((uint32_t*)(ws + p.zero_off), p.zero_words, stream);
+    if (e != hipSuccess) return hip_fail(e, "workspace clear");
+
+    AttnArgs aa{};
+    aa.q = q; aa.q_dtype = q_dtype; aa.k = k; aa.v = v; aa.kv_dtype = kv_dtype;
+    aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = q_pos; aa.kv_len = kv_len;
+    aa.list = nullptr; aa.S = 0; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
+    aa.scale_log2 = scale_log2; aa.nsplit = p.nsplit; aa.chunk = p.chunk;
+    aa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
+    aa.o = o; aa.lse = lse;
+    e = launch_attn_generic(aa, "full_attn_generic", stream);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (p.nsplit > 1) {
+        e = launch_attn_combine(aa, "full_attn_combine", stream);
+        if (e != hipSuccess) return hip_fail(e, "attention combine launch");
+    }
+
+    ScoreArgs sa{};
+    sa.q = q; sa.q_dtype = q_dtype; sa.k = k; sa.kv_dtype = kv_dtype; sa.k_scale = k_scale;
+    sa.q_pos = q_pos; sa.kv_len = kv_len; sa.B = B; sa.Tq = Tq; sa.H = H; sa.d = d; sa.Nmax = Nmax;
+    sa.window = window; sa.scale_log2 = scale_log2; sa.lse = lse; sa.scores = scores; sa.cstride = Nmax;
+    sa.nsplit = p.score_nsplit; sa.chunk = p.score_chunk; sa.rowhist = rowhist;
+    e = launch_score_generic(sa, stream);
+    if (e != hipSuccess) return hip_fail(e, "score launch");
+
+    SelectArgs se{};
+    se.q_pos = q_pos; se.kv_len = kv_len; se.R = (int)p.R; se.Tq = Tq; se.Nmax = Nmax;
+    se.k_global = k_global; se.window = window; se.scores = scores; se.cstride = Nmax;
+    se.rowhist = rowhist; se.counters = counters; se.sure = (int32_t*)(ws + p.off_sure);
+    se.cand = (uint2*)(ws + p.off_cand); se.nseg = p.nseg; se.idx = idx; se.scores_dbg = scores_dbg;
+    e = launch_select(se, /*hist_done=*/true, stream);
+    if (e != hipSuccess) return hip_fail(e, "select launch");
+    return HS2_OK;
+}
+
+size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S) {
+    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || S < 1 || S > 8192) return 0;
+    const size_t n = sparse_ws_bytes((int64_t)B * Tq, H, d, S);
+    return n ? n : kAlign;
+}
+
+hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
+                           const float* k_scale, const float* v_scale, const int32_t* idx, int32_t S,
+                           const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                           float sm_scale, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st != HS2_OK) return st;
+    if (S < 1 || S > 8192) return fail(HS2_ERR_INVALID_ARG, "S=%d outside [1, 8192]", S);
+    if ((int64_t)B * Tq == 0) return HS2_OK;
+    if (!idx) return fail(HS2_ERR_INVALID_ARG, "null idx pointer");
+    const int64_t R = (int64_t)B * Tq;
+    const size_t need = sparse_ws_bytes(R, H, d, S);
+    const bool split = workspace && need > 0 && workspace_bytes >= need;
+
+    AttnArgs aa{};
+    aa.q = q; aa.q_dtype = q_dtype; aa.k = k; aa.v = v; aa.kv_dtype = kv_dtype;
+    aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = nullptr; aa.kv_len = kv_len;
+    aa.list = idx; aa.S = S; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
+    aa.scale_log2 = sm_scale * 1.4426950408889634f;
+    aa.nsplit = split ? sparse_nsplit(R, S) : 1;
+    aa.chunk = ceil_div(ceil_div(S, aa.nsplit), 32) * 32;
+    aa.nsplit = (int)ceil_div(S, aa.chunk);
+    aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
+    aa.o = o; aa.lse = nullptr;
+    hipError_t e = launch_attn_generic(aa, "sparse_attn_generic", stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    if (aa.nsplit > 1) {
+        e = launch_attn_combine(aa, "sparse_attn_combine", stream);
+        if (e != hipSuccess) return hip_fail(e, "sparse combine launch");
+    }
+    return HS2_OK;
+}
+
+}  // extern "C"

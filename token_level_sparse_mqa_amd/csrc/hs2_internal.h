@@ -1,0 +1,84 @@
+// Internal interfaces between the hs2 host code (abi.hip) and the kernel files.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "hs2.h"
+
+namespace hs2 {
+
+// Candidate list capacity per row for the in-LDS selection fast path.
+constexpr int kSelCap = 4096;
+// Radix digits of the fp32 score bit pattern: [31:21] [20:10] [9:0].
+constexpr int kHistBins = 2048;
+// Row segment handled by one select workgroup.
+constexpr int kSelSeg = 4096;
+
+// One attention problem: R = B*Tq query rows, each over a key set given either as the causal
+// range [0, t] (list == nullptr) or as an index list idx[r, 0:S].
+struct AttnArgs {
+    const void* q; int q_dtype;          // [R, H, d]
+    const void* k; const void* v; int kv_dtype;
+    const float* k_scale; const float* v_scale;
+    const int32_t* q_pos;                // [R] (range mode)
+    const int32_t* kv_len;               // [B] or nullptr
+    const int32_t* list; int S;          // [R, S] (list mode)
+    int B, Tq, H, d; int64_t Nmax;
+    float scale_log2;                    // sm_scale * log2(e): logits are kept in base 2
+    int nsplit; int64_t chunk;           // key entries per split
+    float* part;                         // [R, nsplit, H, d + 2]: o, m, l of each split
+    float* o;                            // [R, H, d]
+    float* lse;                          // [R, H] base-2 log-sum-exp (nullptr: not needed)
+};
+
+struct ScoreArgs {
+    const void* q; int q_dtype;
+    const void* k; int kv_dtype; const float* k_scale;
+    const int32_t* q_pos; const int32_t* kv_len;
+    int B, Tq, H, d; int64_t Nmax; int window;
+    float scale_log2;
+    const float* lse;                    // [R, H]
+    float* scores; int64_t cstride;      // [R, cstride]
+    int nsplit; int64_t chunk;
+    uint32_t* rowhist;                   // [R, kHistBins] or nullptr
+};
+
+struct SelectArgs {
+    const int32_t* q_pos; const int32_t* kv_len;
+    int R, Tq; int64_t Nmax; int k_global, window;
+    const float* scores; int64_t cstride;
+    uint32_t* rowhist;                   // [R, kHistBins]
+    uint32_t* counters;                  // [R, 4]: sure count, candidate count
+    int32_t* sure;                       // [R, k_global]
+    uint2* cand;                         // [R, kSelCap] (key bits, index)
+    int nseg;
+    int32_t* idx;                        // [R, k_global + window]
+    float* scores_dbg;                   // [R, Nmax] or nullptr
+};
+
+struct BridgeArgs {
+    const uint16_t* hidden; int64_t T; int D;
+    const uint16_t* wk; const uint16_t* wv; int d;
+    uint16_t* k_out; uint16_t* v_out; int64_t stride;
+};
+
+// Kernel launchers (return the launch status).
+hipError_t launch_attn_generic(const AttnArgs& a, const char* name, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t s);
+hipError_t launch_score_generic(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s);
+hipError_t launch_bridge_generic(const BridgeArgs& a, hipStream_t s);
+
+// Measurement hook: brackets a launch with events on `s` while profiling is enabled.
+struct ProfScope {
+    ProfScope(const char* name, hipStream_t s);
+    ~ProfScope();
+    int slot;
+    hipStream_t stream;
+};
+
+}  // namespace hs2

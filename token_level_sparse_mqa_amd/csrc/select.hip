@@ -1,0 +1,316 @@
+// Token-level top-k selection with a forced recent window.
+//
+// Per query row at position t (kucoin news flash; lynxflow blog, "Token-Level Sparse
+// Selection"): the k_global best candidates j in [0, t - window] by (score desc, index asc),
+// written ascending, then -1 padding; followed by the window max(0, t-window+1)..t and -1
+// padding.  Scores are sums of probabilities, hence >= 0, so their binary32 bit patterns
+// order like the values and an exact radix select over the 32 bits finds the k-th largest
+// score T.  Everything above T is picked; among scores equal to T the lowest indices are
+// picked.  All decisions are taken on the bit patterns: integer work, bit-exact.
+//
+// Kernels (radix digits [31:21] [20:10] [9:0]):
+//   select_hist    per row segment: histogram of the top digit, summed into a row histogram
+//   select_gather  per row segment: entries whose top digit is above the k-th's are sure
+//                  picks; entries in the k-th's bucket become candidates (value, index)
+//   select_finish  per row: resolves the remaining digits and the ties among the candidates
+//                  in LDS, sorts the k picks ascending, writes the window and padding.  When
+//                  the k-th bucket holds more than kSelCap entries it falls back to exact
+//                  streaming passes over the row in global memory.
+#include "hs2_device.h"
+
+namespace hs2 {
+
+__device__ __forceinline__ uint32_t dig1(uint32_t key) { return key >> 21; }
+__device__ __forceinline__ uint32_t dig2(uint32_t key) { return (key >> 10) & 0x7ffu; }
+__device__ __forceinline__ uint32_t dig3(uint32_t key) { return key & 0x3ffu; }
+
+// Given a histogram over nbins digits (LDS) and a rank k (1 <= k <= total), find the digit
+// holding the k-th largest entry and the number of entries with a larger digit.
+// res[0] = digit, res[1] = count above.  All threads of the block call it.
+template <int NT>
+__device__ void find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t* res, uint32_t* tmp) {
+    const int per = (nbins + NT - 1) / NT;
+    const int x0 = threadIdx.x * per;
+    uint32_t local = 0;
+    for (int x = x0; x < x0 + per && x < nbins; ++x) local += hist[nbins - 1 - x];
+    uint32_t total;
+    uint32_t run = block_excl_scan<NT>(local, tmp, &total);
+    for (int x = x0; x < x0 + per && x < nbins; ++x) {
+        const uint32_t c = hist[nbins - 1 - x];
+        if (run < k && run + c >= k) { res[0] = (uint32_t)(nbins - 1 - x); res[1] = run; }
+        run += c;
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void row_info(const SelectArgs& a, int r, int64_t* t, int64_t* C) {
+    *t = row_pos(a.q_pos, a.kv_len, r, a.Tq, a.Nmax);
+    *C = cand_count(*t, a.window);
+}
+
+// Wave-aggregated append: returns the slot of this lane (valid where `pred`).
+__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
+    const uint64_t m = __ballot(pred);
+    if (!m) return 0;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((unsigned long long)m) - 1;
+    uint32_t base = 0;
+    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
+    base = __shfl(base, leader);
+    return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
+}
+
+__global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
+    __shared__ uint32_t hist[kHistBins];
+    const int r = blockIdx.x, seg = blockIdx.y;
+    int64_t t, C;
+    row_info(a, r, &t, &C);
+    if (C <= a.k_global) return;
+    const int64_t j0 = (int64_t)seg * kSelSeg;
+    if (j0 >= C) return;
+    const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
+    for (int x = threadIdx.x; x < kHistBins; x += 256) hist[x] = 0;
+    __syncthreads();
+    const float* sc = a.scores + (int64_t)r * a.cstride;
+    for (int64_t j = j0 + threadIdx.x; j < j1; j += 256) atomicAdd(&hist[dig1(__float_as_uint(sc[j]))], 1u);
+    __syncthreads();
+    for (int x = threadIdx.x; x < kHistBins; x += 256)
+        if (hist[x]) atomicAdd(&a.rowhist[(int64_t)r * kHistBins + x], hist[x]);
+}
+
+__global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t tmp[8];
+    __shared__ uint32_t res[2];
+    const int r = blockIdx.x, seg = blockIdx.y;
+    int64_t t, C;
+    row_info(a, r, &t, &C);
+    if (C <= a.k_global) return;
+    const int64_t j0 = (int64_t)seg * kSelSeg;
+    if (j0 >= C) return;
+    const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
+    for (int x = threadIdx.x; x < kHistBins; x += 256) hist[x] = a.rowhist[(int64_t)r * kHistBins + x];
+    __syncthreads();
+    find_digit<256>(hist, kHistBins, (uint32_t)a.k_global, res, tmp);
+    const uint32_t b1 = res[0];
+    const float* sc = a.scores + (int64_t)r * a.cstride;
+    uint32_t* cnt = a.counters + (int64_t)r * 4;
+    for (int64_t jb = j0; jb < j1; jb += 256) {
+        const int64_t j = jb + threadIdx.x;
+        uint32_t key = 0, dg = 0;
+        const bool in = j < j1;
+        if (in) { key = __float_as_uint(sc[j]); dg = dig1(key); }
+        const bool sure = in && dg > b1;
+        const bool cand = in && dg == b1;
+        const uint32_t ps = wave_append(&cnt[0], sure);
+        if (sure) a.sure[(int64_t)r * a.k_global + ps] = (int32_t)j;
+        const uint32_t pc = wave_append(&cnt[1], cand);
+        if (cand && pc < (uint32_t)kSelCap) a.cand[(int64_t)r * kSelCap + pc] = make_uint2(key, (uint32_t)j);
+    }
+}
+
+constexpr int kFinThreads = 1024;
+
+// Ascending bitonic sort of n (power of two) 32-bit values in LDS.
+__device__ void bitonic_sort_i32(int32_t* v, int n) {
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            for (int i = threadIdx.x; i < n; i += kFinThreads) {
+                const int ixj = i ^ j;
+                if (ixj > i) {
+                    const int32_t x = v[i], y = v[ixj];
+                    const bool up = (i & k) == 0;
+                    if ((x > y) == up) { v[i] = y; v[ixj] = x; }
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a) {
+    __shared__ uint32_t hist[kHistBins];
+    __shared__ uint32_t ckey[kSelCap];
+    __shared__ int32_t cidx[kSelCap];
+    __shared__ int32_t out[4096];
+    __shared__ uint32_t tmp[kFinThreads / 64 + 1];
+    __shared__ uint32_t res[2];
+    __shared__ uint32_t lcount[2];
+
+    const int r = blockIdx.x;
+    const int K = a.k_global, W = a.window;
+    int64_t t, C;
+    row_info(a, r, &t, &C);
+    int32_t* irow = a.idx + (int64_t)r * (K + W);
+    const float* sc = a.scores + (int64_t)r * a.cstride;
+
+    // window segment and the optional score dump
+    for (int w = threadIdx.x; w < W; w += kFinThreads) {
+        const int64_t j = t - W + 1 + w;
+        int32_t v = -1;
+        if (t >= 0) {
+            const int64_t first = t - W + 1 > 0 ? t - W + 1 : 0;
+            const int64_t jj = first + w;
+            v = jj <= t ? (int32_t)jj : -1;
+        }
+        (void)j;
+        irow[K + w] = v;
+    }
+    if (a.scores_dbg) {
+        float* dbg = a.scores_dbg + (int64_t)r * a.Nmax;
+        for (int64_t j = threadIdx.x; j < a.Nmax; j += kFinThreads) dbg[j] = j < C ? sc[j] : -1.0f;
+    }
+    if (C <= K) {
+        for (int j = threadIdx.x; j < K; j += kFinThreads) irow[j] = j < C ? j : -1;
+        return;
+    }
+
+    for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = a.rowhist[(int64_t)r * kHistBins + x];
+    __syncthreads();
+    find_digit<kFinThreads>(hist, kHistBins, (uint32_t)K, res, tmp);
+    const uint32_t b1 = res[0], above1 = res[1];
+    const uint32_t k1 = (uint32_t)K - above1;
+    const uint32_t* cnt = a.counters + (int64_t)r * 4;
+    const uint32_t n_cand = cnt[1];
+    uint32_t b2, b3, above2, above3;
+
+    if (n_cand <= (uint32_t)kSelCap) {
+        // ---- fast path: the k-th bucket is in LDS ----
+        const uint2* cg = a.cand + (int64_t)r * kSelCap;
+        for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads) { const uint2 e = cg[x]; ckey[x] = e.x; cidx[x] = (int32_t)e.y; }
+        for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
+        __syncthreads();
+        for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads) atomicAdd(&hist[dig2(ckey[x])], 1u);
+        __syncthreads();
+        find_digit<kFinThreads>(hist, kHistBins, k1, res, tmp);
+        b2 = res[0]; above2 = res[1];
+        const uint32_t k2 = k1 - above2;
+        for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
+        __syncthreads();
+        for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads)
+            if (dig2(ckey[x]) == b2) atomicAdd(&hist[dig3(ckey[x])], 1u);
+        __syncthreads();
+        find_digit<kFinThreads>(hist, 1024, k2, res, tmp);
+        b3 = res[0]; above3 = res[1];
+        const uint32_t need_eq = k2 - above3;          // ties at T still needed
+        const uint32_t n_eq = hist[b3];
+        const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
+        // sure picks from the gather pass
+        const uint32_t n_sure = above1;
+        for (uint32_t x = threadIdx.x; x < n_sure; x += kFinThreads) out[x] = a.sure[(int64_t)r * K + x];
+        if (threadIdx.x == 0) { lcount[0] = n_sure; lcount[1] = 0; }
+        // classify the bucket: above T -> picked; equal to T -> tie list (reusing ckey storage)
+        uint32_t myk[kSelCap / kFinThreads];
+        int32_t myi[kSelCap / kFinThreads];
+#pragma unroll
+        for (int u = 0; u < kSelCap / kFinThreads; ++u) {
+            const uint32_t x = threadIdx.x + u * kFinThreads;
+            myk[u] = x < n_cand ? ckey[x] : 0u;
+            myi[u] = x < n_cand ? cidx[x] : -1;
+        }
+        __syncthreads();
+        int32_t* ties = (int32_t*)ckey;
+#pragma unroll
+        for (int u = 0; u < kSelCap / kFinThreads; ++u) {
+            const uint32_t x = threadIdx.x + u * kFinThreads;
+            if (x < n_cand) {
+                if (myk[u] > T) out[atomicAdd(&lcount[0], 1u)] = myi[u];
+                else if (myk[u] == T) ties[atomicAdd(&lcount[1], 1u)] = myi[u];
+            }
+        }
+        __syncthreads();
+        const uint32_t base = lcount[0];
+        if (need_eq == n_eq) {
+            for (uint32_t x = threadIdx.x; x < n_eq; x += kFinThreads) out[base + x] = ties[x];
+        } else {
+            int np = 1;
+            while (np < (int)n_eq) np <<= 1;
+            for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= (int)n_eq) ties[x] = 0x7fffffff;
+            __syncthreads();
+            bitonic_sort_i32(ties, np);
+            for (uint32_t x = threadIdx.x; x < need_eq; x += kFinThreads) out[base + x] = ties[x];
+        }
+        __syncthreads();
+        int np = 1;
+        while (np < K) np <<= 1;
+        for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= K) out[x] = 0x7fffffff;
+        __syncthreads();
+        bitonic_sort_i32(out, np);
+        for (int x = threadIdx.x; x < K; x += kFinThreads) irow[x] = out[x];
+        return;
+    }
+
+    // ---- fallback: exact streaming passes over the row ----
+    for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
+    __syncthreads();
+    for (int64_t j = threadIdx.x; j < C; j += kFinThreads) {
+        const uint32_t key = __float_as_uint(sc[j]);
+        if (dig1(key) == b1) atomicAdd(&hist[dig2(key)], 1u);
+    }
+    __syncthreads();
+    find_digit<kFinThreads>(hist, kHistBins, k1, res, tmp);
+    b2 = res[0]; above2 = res[1];
+    const uint32_t k2 = k1 - above2;
+    const uint32_t pre = (b1 << 11) | b2;
+    for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
+    __syncthreads();
+    for (int64_t j = threadIdx.x; j < C; j += kFinThreads) {
+        const uint32_t key = __float_as_uint(sc[j]);
+        if ((key >> 10) == pre) atomicAdd(&hist[dig3(key)], 1u);
+    }
+    __syncthreads();
+    find_digit<kFinThreads>(hist, 1024, k2, res, tmp);
+    b3 = res[0]; above3 = res[1];
+    const uint32_t need_eq = k2 - above3;
+    const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
+    // ordered pass: ties ranked by index with a running block scan
+    uint32_t run_eq = 0, run_out = 0;
+    for (int64_t jb = 0; jb < C; jb += kFinThreads) {
+        const int64_t j = jb + threadIdx.x;
+        uint32_t key = 0;
+        if (j < C) key = __float_as_uint(sc[j]);
+        const bool eq = j < C && key == T;
+        uint32_t tot_eq;
+        const uint32_t rank = run_eq + block_excl_scan<kFinThreads>(eq ? 1u : 0u, tmp, &tot_eq);
+        const bool pick = j < C && (key > T || (eq && rank < need_eq));
+        uint32_t tot_pick;
+        const uint32_t pos = run_out + block_excl_scan<kFinThreads>(pick ? 1u : 0u, tmp, &tot_pick);
+        if (pick) irow[pos] = (int32_t)j;
+        run_eq += tot_eq;
+        run_out += tot_pick;
+    }
+}
+
+__global__ void zero_u32_kernel(uint32_t* p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
+    ProfScope ps("zero", s);
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks == 0) return hipSuccess;
+    zero_u32_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
+    dim3 grid(a.R, a.nseg);
+    if (!hist_done) {
+        ProfScope ps("select_hist", s);
+        select_hist_kernel<<<grid, 256, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    {
+        ProfScope ps("select_gather", s);
+        select_gather_kernel<<<grid, 256, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    ProfScope ps("select_finish", s);
+    select_finish_kernel<<<a.R, kFinThreads, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace hs2

@@ -126,6 +126,8 @@ def _needle_plan(cfg: Config) -> List[Tuple[int, int, int, int]]:
         sp, sq = t0 // 64, cfg.Tq // 64
         for i in range(64):
             plan.append((0, t0 + sq * i + sq - 1, i % cfg.H, sp * i + sp // 2))
+    for (_, t, _, p) in plan:
+        assert p <= t - cfg.window, "a needle must be a global candidate of its query"
     return plan
 
 
