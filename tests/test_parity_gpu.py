@@ -170,9 +170,7 @@ def test_bridge_strided_rows():
     c = bits_from_dev(cache)
     ko, vo = oracle.kv_bridge(hb, wkb, wvb)
     assert np.all(oracle.decode(c[:, :d], "bf16") == -7.0)
-    ulp_k = np.abs(c[:, d:2 * d].astype(np.int32) - ko.astype(np.int32))
-    ulp_v = np.abs(c[:, 2 * d:].astype(np.int32) - vo.astype(np.int32))
-    assert ulp_k.max() <= 1 and ulp_v.max() <= 1
+    check_bridge(hb, wkb, wvb, np.ascontiguousarray(c[:, d:2 * d]), np.ascontiguousarray(c[:, 2 * d:]), ko, vo)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -210,10 +208,26 @@ def test_full_prefill_chunk_sampled():
 def test_full_prefill_exit256k_sampled():
     cfg = CONFIGS["prefill_exit256k"]
     g, wl, _, O = run_parity(cfg, rows=_sample_rows(cfg, [], n_extra=4), check_scores=False)
-    # the bridge itself: within one bf16 ulp of the float64 projection, mismatch fraction reported
+    # the bridge itself against the float64 projection
     kb, vb = bits_from_dev(g.k[0]), bits_from_dev(g.v[0])
-    ko, vo = O.k_bits, O.v_bits
-    dk = np.abs(kb.astype(np.int32) - ko.astype(np.int32))
-    dv = np.abs(vb.astype(np.int32) - vo.astype(np.int32))
-    _say(f"[parity] bridge mismatch fraction K {np.mean(dk > 0):.2e} V {np.mean(dv > 0):.2e}")
-    assert dk.max() <= 1 and dv.max() <= 1
+    check_bridge(wl.hidden, wl.wk, wl.wv, kb, vb, O.k_bits, O.v_bits)
+
+
+def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0):
+    """GPU bridge output vs the oracle's: the bit patterns may differ only where fp32 summation
+    can move the sum across a bf16 rounding boundary.  Bound per element (sampled rows):
+    |gpu - exact| <= D * 2^-24 * sum_i |h_i w_i| + one bf16 ulp of the exact value."""
+    import oracle
+    D = hidden.shape[1]
+    frac_k, frac_v = float(np.mean(kb != ko)), float(np.mean(vb != vo))
+    _say(f"[parity] bridge mismatch fraction K {frac_k:.2e} V {frac_v:.2e}")
+    assert frac_k < 1e-3 and frac_v < 1e-3
+    rows = np.random.default_rng(seed).choice(hidden.shape[0], size=min(sample, hidden.shape[0]), replace=False)
+    h = oracle.decode(hidden[rows], "bf16")
+    for w_bits, got in ((wk, kb), (wv, vb)):
+        w = oracle.decode(w_bits, "bf16")
+        exact = h @ w
+        mag = np.abs(h) @ np.abs(w)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
+        err = np.abs(oracle.decode(got[rows], "bf16") - exact)
+        assert np.all(err <= D * 2.0 ** -24 * mag + ulp)
