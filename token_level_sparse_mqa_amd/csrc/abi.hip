@@ -39,7 +39,10 @@ bool dtype_pair_ok(int qd, int kd) {
 }
 
 // ---- workspace plan of hs2_full_attn_select ----------------------------------------------------
+enum Path { PATH_GENERIC = 0, PATH_MFMA_ROWS = 1 };
+
 struct SelectPlan {
+    Path path;
     int64_t R;
     int nsplit; int64_t chunk;         // attention pass over keys
     int score_nsplit; int64_t score_chunk;
@@ -48,18 +51,32 @@ struct SelectPlan {
     size_t zero_off, zero_words;       // rowhist + counters, cleared at the start of a call
 };
 
-SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global) {
-    SelectPlan p{};
-    p.R = (int64_t)B * Tq;
-    // enough workgroups to fill 256 CUs several times over, at least 256 keys per split
-    int64_t ns = ceil_div(4096, p.R);
-    const int64_t ns_max = ceil_div(Nmax, 256);
+// Split a key range of n entries over workgroups: at least `min_chunk` entries each (a multiple
+// of `quant`), and about `target_wg` workgroups over all R rows.
+void split_range(int64_t R, int64_t n, int64_t target_wg, int64_t min_chunk, int64_t quant,
+                 int* nsplit, int64_t* chunk) {
+    int64_t ns = ceil_div(target_wg, R);
+    const int64_t ns_max = ceil_div(n, min_chunk);
     if (ns > ns_max) ns = ns_max;
     if (ns < 1) ns = 1;
-    p.nsplit = (int)ns;
-    p.chunk = ceil_div(ceil_div(Nmax, ns), 32) * 32;
-    p.score_nsplit = p.nsplit;
-    p.score_chunk = p.chunk;
+    int64_t c = ceil_div(ceil_div(n, ns), quant) * quant;
+    *chunk = c;
+    *nsplit = (int)ceil_div(n, c);
+}
+
+SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, int kv_dtype) {
+    SelectPlan p{};
+    p.R = (int64_t)B * Tq;
+    p.path = kv_dtype == HS2_F32 ? PATH_GENERIC : PATH_MFMA_ROWS;
+    if (p.path == PATH_GENERIC) {
+        split_range(p.R, Nmax, 4096, 256, 32, &p.nsplit, &p.chunk);
+        p.score_nsplit = p.nsplit;
+        p.score_chunk = p.chunk;
+    } else {
+        const int64_t min_chunk = kv_dtype == HS2_FP8_E4M3 ? 2048 : 1024;
+        split_range(p.R, Nmax, 1024, min_chunk, 128, &p.nsplit, &p.chunk);
+        split_range(p.R, Nmax, 1024, min_chunk, 128, &p.score_nsplit, &p.score_chunk);
+    }
     p.nseg = (int)ceil_div(Nmax, kSelSeg);
     size_t off = 0;
     p.off_part = off;   off = align_up(off + (p.nsplit > 1 ? (size_t)p.R * p.nsplit * H * (d + 2) * 4 : 0));
@@ -75,15 +92,14 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global) 
     return p;
 }
 
-int sparse_nsplit(int64_t R, int S) {
-    int64_t ns = ceil_div(2048, R);
-    const int64_t ns_max = ceil_div(S, 64);
-    if (ns > ns_max) ns = ns_max;
-    return ns < 1 ? 1 : (int)ns;
+void sparse_plan(int64_t R, int S, int q_dtype, int* nsplit, int64_t* chunk) {
+    if (q_dtype == HS2_F32) split_range(R, S, 2048, 64, 32, nsplit, chunk);
+    else split_range(R, S, 1024, 128, 128, nsplit, chunk);
 }
 
-size_t sparse_ws_bytes(int64_t R, int H, int d, int S) {
-    const int ns = sparse_nsplit(R, S);
+size_t sparse_ws_bytes(int64_t R, int H, int d, int S, int q_dtype) {
+    int ns; int64_t c;
+    sparse_plan(R, S, q_dtype, &ns, &c);
     return ns > 1 ? (size_t)R * ns * H * (d + 2) * 4 : 0;
 }
 
@@ -203,11 +219,11 @@ hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D, const void* w
 
 size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
                                            int32_t k_global, int32_t window, hs2_dtype kv_dtype) {
-    (void)kv_dtype; (void)window;
+    (void)window;
     if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 || k_global < 1 || k_global > 4096)
         return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
-    return plan_select(B, Tq, H, d, Nmax, k_global).total;
+    return plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype).total;
 }
 
 hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
@@ -221,7 +237,7 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
     if ((int64_t)B * Tq == 0) return HS2_OK;
     if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
-    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global);
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
     if (!workspace || workspace_bytes < p.total)
         return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
 
@@ -242,19 +258,23 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     aa.scale_log2 = scale_log2; aa.nsplit = p.nsplit; aa.chunk = p.chunk;
     aa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
     aa.o = o; aa.lse = lse;
-    e = launch_attn_generic(aa, "full_attn_generic", stream);
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
-    if (p.nsplit > 1) {
-        e = launch_attn_combine(aa, "full_attn_combine", stream);
-        if (e != hipSuccess) return hip_fail(e, "attention combine launch");
+    if (p.path == PATH_GENERIC) {
+        e = launch_attn_generic(aa, "full_attn_generic", stream);
+        if (e != hipSuccess) return hip_fail(e, "attention launch");
+        if (p.nsplit > 1) e = launch_attn_combine(aa, "full_attn_combine", stream);
+    } else {
+        e = launch_attn_rows_mfma(aa, "full_attn_mfma", stream);
+        if (e != hipSuccess) return hip_fail(e, "attention launch");
+        if (p.nsplit > 1) e = launch_attn_split_combine(aa, "full_attn_combine", stream);
     }
+    if (e != hipSuccess) return hip_fail(e, "attention combine launch");
 
     ScoreArgs sa{};
     sa.q = q; sa.q_dtype = q_dtype; sa.k = k; sa.kv_dtype = kv_dtype; sa.k_scale = k_scale;
     sa.q_pos = q_pos; sa.kv_len = kv_len; sa.B = B; sa.Tq = Tq; sa.H = H; sa.d = d; sa.Nmax = Nmax;
     sa.window = window; sa.scale_log2 = scale_log2; sa.lse = lse; sa.scores = scores; sa.cstride = Nmax;
     sa.nsplit = p.score_nsplit; sa.chunk = p.score_chunk; sa.rowhist = rowhist;
-    e = launch_score_generic(sa, stream);
+    e = p.path == PATH_GENERIC ? launch_score_generic(sa, stream) : launch_score_rows_mfma(sa, stream);
     if (e != hipSuccess) return hip_fail(e, "score launch");
 
     SelectArgs se{};
@@ -269,7 +289,10 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
 
 size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S) {
     if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || S < 1 || S > 8192) return 0;
-    const size_t n = sparse_ws_bytes((int64_t)B * Tq, H, d, S);
+    // the workspace is sized for the larger of the fp32 and bf16 plans
+    size_t n = sparse_ws_bytes((int64_t)B * Tq, H, d, S, HS2_F32);
+    const size_t n2 = sparse_ws_bytes((int64_t)B * Tq, H, d, S, HS2_BF16);
+    if (n2 > n) n = n2;
     return n ? n : kAlign;
 }
 
@@ -283,7 +306,7 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
     if ((int64_t)B * Tq == 0) return HS2_OK;
     if (!idx) return fail(HS2_ERR_INVALID_ARG, "null idx pointer");
     const int64_t R = (int64_t)B * Tq;
-    const size_t need = sparse_ws_bytes(R, H, d, S);
+    const size_t need = sparse_ws_bytes(R, H, d, S, q_dtype);
     const bool split = workspace && need > 0 && workspace_bytes >= need;
 
     AttnArgs aa{};
@@ -291,17 +314,25 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
     aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = nullptr; aa.kv_len = kv_len;
     aa.list = idx; aa.S = S; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
     aa.scale_log2 = sm_scale * 1.4426950408889634f;
-    aa.nsplit = split ? sparse_nsplit(R, S) : 1;
-    aa.chunk = ceil_div(ceil_div(S, aa.nsplit), 32) * 32;
-    aa.nsplit = (int)ceil_div(S, aa.chunk);
+    if (split) {
+        sparse_plan(R, S, q_dtype, &aa.nsplit, &aa.chunk);
+    } else {
+        aa.nsplit = 1;
+        aa.chunk = S;
+    }
     aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
     aa.o = o; aa.lse = nullptr;
-    hipError_t e = launch_attn_generic(aa, "sparse_attn_generic", stream);
-    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
-    if (aa.nsplit > 1) {
-        e = launch_attn_combine(aa, "sparse_attn_combine", stream);
-        if (e != hipSuccess) return hip_fail(e, "sparse combine launch");
+    hipError_t e;
+    if (q_dtype == HS2_F32) {
+        e = launch_attn_generic(aa, "sparse_attn_generic", stream);
+        if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+        if (aa.nsplit > 1) e = launch_attn_combine(aa, "sparse_attn_combine", stream);
+    } else {
+        e = launch_attn_rows_mfma(aa, "sparse_attn_mfma", stream);
+        if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+        if (aa.nsplit > 1) e = launch_attn_split_combine(aa, "sparse_attn_combine", stream);
     }
+    if (e != hipSuccess) return hip_fail(e, "sparse combine launch");
     return HS2_OK;
 }
 
