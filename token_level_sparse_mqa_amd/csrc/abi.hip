@@ -320,10 +320,13 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
         aa.nsplit = 1;
         aa.chunk = S;
     }
+    // the MFMA kernel stages at most 1280 list entries per workgroup; longer unsplit lists
+    // take the generic kernel
+    const bool mfma = q_dtype != HS2_F32 && aa.chunk <= 1280;
     aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
     aa.o = o; aa.lse = nullptr;
     hipError_t e;
-    if (q_dtype == HS2_F32) {
+    if (!mfma) {
         e = launch_attn_generic(aa, "sparse_attn_generic", stream);
         if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
         if (aa.nsplit > 1) e = launch_attn_combine(aa, "sparse_attn_combine", stream);

@@ -78,10 +78,14 @@ __global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
         if (hist[x]) atomicAdd(&a.rowhist[(int64_t)r * kHistBins + x], hist[x]);
 }
 
+// Each workgroup counts its sure picks and bucket candidates, reserves space for them with one
+// atomic per counter, then writes them (per-row counters stay uncontended).
 __global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
+    constexpr int PER = kSelSeg / 256;
     __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t tmp[8];
     __shared__ uint32_t res[2];
+    __shared__ uint32_t basev[2];
     const int r = blockIdx.x, seg = blockIdx.y;
     int64_t t, C;
     row_info(a, r, &t, &C);
@@ -94,18 +98,37 @@ __global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
     find_digit<256>(hist, kHistBins, (uint32_t)a.k_global, res, tmp);
     const uint32_t b1 = res[0];
     const float* sc = a.scores + (int64_t)r * a.cstride;
+    uint32_t key[PER];
+    uint32_t ns = 0, nc = 0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int64_t j = j0 + u * 256 + threadIdx.x;
+        key[u] = j < j1 ? __float_as_uint(sc[j]) : 0u;
+        const uint32_t dg = dig1(key[u]);
+        ns += (j < j1 && dg > b1) ? 1u : 0u;
+        nc += (j < j1 && dg == b1) ? 1u : 0u;
+    }
+    uint32_t tot_s, tot_c;
+    uint32_t ps = block_excl_scan<256>(ns, tmp, &tot_s);
+    uint32_t pc = block_excl_scan<256>(nc, tmp, &tot_c);
     uint32_t* cnt = a.counters + (int64_t)r * 4;
-    for (int64_t jb = j0; jb < j1; jb += 256) {
-        const int64_t j = jb + threadIdx.x;
-        uint32_t key = 0, dg = 0;
-        const bool in = j < j1;
-        if (in) { key = __float_as_uint(sc[j]); dg = dig1(key); }
-        const bool sure = in && dg > b1;
-        const bool cand = in && dg == b1;
-        const uint32_t ps = wave_append(&cnt[0], sure);
-        if (sure) a.sure[(int64_t)r * a.k_global + ps] = (int32_t)j;
-        const uint32_t pc = wave_append(&cnt[1], cand);
-        if (cand && pc < (uint32_t)kSelCap) a.cand[(int64_t)r * kSelCap + pc] = make_uint2(key, (uint32_t)j);
+    if (threadIdx.x == 0) {
+        basev[0] = tot_s ? atomicAdd(&cnt[0], tot_s) : 0u;
+        basev[1] = tot_c ? atomicAdd(&cnt[1], tot_c) : 0u;
+    }
+    __syncthreads();
+    ps += basev[0];
+    pc += basev[1];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int64_t j = j0 + u * 256 + threadIdx.x;
+        if (j >= j1) continue;
+        const uint32_t dg = dig1(key[u]);
+        if (dg > b1) a.sure[(int64_t)r * a.k_global + ps++] = (int32_t)j;
+        else if (dg == b1) {
+            if (pc < (uint32_t)kSelCap) a.cand[(int64_t)r * kSelCap + pc] = make_uint2(key[u], (uint32_t)j);
+            ++pc;
+        }
     }
 }
 
@@ -126,6 +149,31 @@ __device__ void bitonic_sort_i32(int32_t* v, int n) {
             __syncthreads();
         }
     }
+}
+
+// Ascending bitonic sort of n <= kFinThreads values, one per thread (thread i holds element i);
+// exchanges between lanes of a wave use shuffles, wider ones go through `buf` in LDS.
+// Returns this thread's element of the sorted sequence.
+__device__ int32_t bitonic_sort_1pt(int32_t v, int n, int32_t* buf) {
+    const int i = threadIdx.x;
+    for (int k = 2; k <= n; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            int32_t other;
+            if (j >= 64) {
+                __syncthreads();
+                if (i < n) buf[i] = v;
+                __syncthreads();
+                other = (i < n) ? buf[i ^ j] : v;
+            } else {
+                other = __shfl_xor(v, j);
+            }
+            const bool up = (i & k) == 0;
+            const bool lower = (i & j) == 0;
+            if (i < n) v = (lower == up) ? min(v, other) : max(v, other);
+        }
+    }
+    __syncthreads();
+    return v;
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a) {
@@ -235,8 +283,13 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         while (np < K) np <<= 1;
         for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= K) out[x] = 0x7fffffff;
         __syncthreads();
-        bitonic_sort_i32(out, np);
-        for (int x = threadIdx.x; x < K; x += kFinThreads) irow[x] = out[x];
+        if (np <= kFinThreads) {
+            const int32_t v = bitonic_sort_1pt(threadIdx.x < np ? out[threadIdx.x] : 0x7fffffff, np, out);
+            if (threadIdx.x < K) irow[threadIdx.x] = v;
+        } else {
+            bitonic_sort_i32(out, np);
+            for (int x = threadIdx.x; x < K; x += kFinThreads) irow[x] = out[x];
+        }
         return;
     }
 
