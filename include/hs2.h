@@ -41,10 +41,12 @@
  *    o: [B, Tq, H, d] fp32; idx: [B, Tq, k_global + window] int32.
  *  - Supported: d in {64, 128}; 1 <= H <= 32; (q, kv) dtypes (F32, F32), (BF16, BF16) and
  *    (BF16, FP8_E4M3).  Other combinations return HS2_ERR_UNSUPPORTED.
- *  - BF16/FP8 paths run on bf16 MFMA with fp32 accumulation: Q.K^T on the exact bf16 values
- *    (FP8 codes convert to bf16 exactly), and the attention weights split into a bf16 high and
- *    low part against bf16 V (weights kept to about 2^-16 relative).  fp32 paths compute in
- *    fp32 throughout.
+ *  - BF16/FP8 paths run on MFMA with fp32 accumulation.  Q.K^T uses the exact bf16 values
+ *    (FP8 codes convert to bf16 exactly).  For P.V, calls with Tq < 8 query tokens per
+ *    sequence (decode) and hs2_sparse_attn split the attention weights into a bf16 high and
+ *    low part against bf16 V (weights kept to about 2^-16 relative); calls with Tq >= 8
+ *    (query chunks) use fp16 weights against V converted to fp16, which is exact for bf16 V
+ *    with |v| <= 65504 (larger values saturate).  fp32 paths compute in fp32 throughout.
  */
 #ifndef HS2_H
 #define HS2_H

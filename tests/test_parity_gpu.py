@@ -95,6 +95,11 @@ SMALL = [
     small_config("all_ties_small", 212, B=1, N=2000, Tq=2, n_sparse=1, ident_keys=True),
     # small k and window
     small_config("k16_w4", 213, B=2, N=777, Tq=3, n_sparse=1, k_global=16, window=4),
+    # query-chunk kernels: ragged workgroups, d=64, FP8, several sequences
+    small_config("chunk_h16_d64", 215, B=2, N=2900, Tq=40, H=16, d=64, n_sparse=1),
+    small_config("chunk_fp8", 216, B=1, N=3001, Tq=24, kv_dtype="fp8", n_sparse=1),
+    small_config("chunk_ragged", 217, B=2, N=2000, Tq=13, n_sparse=1),
+    small_config("chunk_k16_w4", 218, B=1, N=500, Tq=16, n_sparse=1, k_global=16, window=4),
 ]
 
 

@@ -39,7 +39,10 @@ bool dtype_pair_ok(int qd, int kd) {
 }
 
 // ---- workspace plan of hs2_full_attn_select ----------------------------------------------------
-enum Path { PATH_GENERIC = 0, PATH_MFMA_ROWS = 1 };
+enum Path { PATH_GENERIC = 0, PATH_MFMA_ROWS = 1, PATH_MFMA_PREFILL = 2 };
+// query tokens per sequence from which the chunk kernels (8 queries sharing each K/V tile)
+// replace the one-row-per-workgroup kernels
+constexpr int kPrefillMinTq = 8;
 
 struct SelectPlan {
     Path path;
@@ -67,8 +70,11 @@ void split_range(int64_t R, int64_t n, int64_t target_wg, int64_t min_chunk, int
 SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, int kv_dtype) {
     SelectPlan p{};
     p.R = (int64_t)B * Tq;
-    p.path = kv_dtype == HS2_F32 ? PATH_GENERIC : PATH_MFMA_ROWS;
-    if (p.path == PATH_GENERIC) {
+    p.path = kv_dtype == HS2_F32 ? PATH_GENERIC : (Tq >= kPrefillMinTq ? PATH_MFMA_PREFILL : PATH_MFMA_ROWS);
+    if (p.path == PATH_MFMA_PREFILL) {
+        p.nsplit = 1; p.chunk = Nmax;
+        p.score_nsplit = 1; p.score_chunk = Nmax;
+    } else if (p.path == PATH_GENERIC) {
         split_range(p.R, Nmax, 4096, 256, 32, &p.nsplit, &p.chunk);
         p.score_nsplit = p.nsplit;
         p.score_chunk = p.chunk;
@@ -262,6 +268,8 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
         e = launch_attn_generic(aa, "full_attn_generic", stream);
         if (e != hipSuccess) return hip_fail(e, "attention launch");
         if (p.nsplit > 1) e = launch_attn_combine(aa, "full_attn_combine", stream);
+    } else if (p.path == PATH_MFMA_PREFILL) {
+        e = launch_attn_prefill(aa, stream);
     } else {
         e = launch_attn_rows_mfma(aa, "full_attn_mfma", stream);
         if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -274,7 +282,8 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     sa.q_pos = q_pos; sa.kv_len = kv_len; sa.B = B; sa.Tq = Tq; sa.H = H; sa.d = d; sa.Nmax = Nmax;
     sa.window = window; sa.scale_log2 = scale_log2; sa.lse = lse; sa.scores = scores; sa.cstride = Nmax;
     sa.nsplit = p.score_nsplit; sa.chunk = p.score_chunk; sa.rowhist = rowhist;
-    e = p.path == PATH_GENERIC ? launch_score_generic(sa, stream) : launch_score_rows_mfma(sa, stream);
+    e = p.path == PATH_GENERIC ? launch_score_generic(sa, stream)
+        : p.path == PATH_MFMA_PREFILL ? launch_score_prefill(sa, stream) : launch_score_rows_mfma(sa, stream);
     if (e != hipSuccess) return hip_fail(e, "score launch");
 
     SelectArgs se{};

@@ -1,0 +1,403 @@
+// MFMA kernels for query chunks (prefill): the full-attention pass and the score pass.
+//
+// A chunk of new tokens attends causally over the cache (agentik-os article, section 1: a long
+// observation is prefilled into a growing context).  MQA lets the eight query tokens of a
+// workgroup share every K/V tile: the tile is read from memory once into LDS and all eight
+// waves (one query token each, its 32 heads as the MFMA N dimension) multiply against it.
+//
+// Pass 1 per wave and 32-key tile:
+//   S^T = K_tile . Q^T (bf16 MFMA), causal mask key <= t, online softmax in base 2,
+//   O^T += V^T . P^T with V staged in LDS as fp16 and P rounded to fp16 (fp16 MFMA).
+// Pass 2 (score) per wave and tile:
+//   S = Q . K_tile^T, score(j) = sum_h 2^(x_h(j) - lse_h), a per-row radix histogram in LDS.
+//
+// Workgroup tiles are double-buffered in LDS; the cooperative global loads of the next tiles
+// are kept in flight in registers (unconditional, clamped loads) while a tile is computed.
+#include "mfma_tiles.h"
+
+namespace hs2 {
+
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+
+constexpr int kPfWaves = 8;                  // query tokens (waves) per workgroup
+constexpr int kPfThreads = kPfWaves * 64;
+
+// Geometry of the cooperative (workgroup-wide) loads of one tile in storage format.
+template <int D, int KV>
+struct PfGeom {
+    using G = RawGeom<D, KV>;
+    static constexpr int CHUNKS = kTileRows * G::CPR;                    // 16-byte chunks per tile
+    static constexpr int NX = (CHUNKS + kPfThreads - 1) / kPfThreads;    // loads per thread
+};
+
+template <int D, int KV>
+__device__ __forceinline__ void pf_load(u32x4_t* raw, const void* base, int64_t rowbase, int64_t k0, int64_t khi) {
+    using G = RawGeom<D, KV>;
+    using P = PfGeom<D, KV>;
+#pragma unroll
+    for (int x = 0; x < P::NX; ++x) {
+        int q = threadIdx.x + x * kPfThreads;
+        q = q < P::CHUNKS ? q : P::CHUNKS - 1;
+        const int R = q / G::CPR, c = q % G::CPR;
+        const int64_t key = k0 + R < khi ? k0 + R : khi - 1;
+        raw[x] = *(const u32x4_t*)((const char*)base + (rowbase + key) * G::RB + 16 * c);
+    }
+}
+
+// bf16 LDS tile from raw K (FP8 codes converted exactly).
+template <int D, int KV>
+__device__ __forceinline__ void pf_store_k(const u32x4_t* raw, char* lds) {
+    using G = RawGeom<D, KV>;
+    using P = PfGeom<D, KV>;
+    using T = LdsTile<D>;
+#pragma unroll
+    for (int x = 0; x < P::NX; ++x) {
+        const int q = threadIdx.x + x * kPfThreads;
+        if (q >= P::CHUNKS) continue;
+        const int R = q / G::CPR, c = q % G::CPR;
+        if (KV == HS2_FP8_E4M3) {
+            u32x4_t lo, hi;
+            const u32x2_t a = fp8x4_to_bf16x4(raw[x][0]), b = fp8x4_to_bf16x4(raw[x][1]);
+            const u32x2_t cc = fp8x4_to_bf16x4(raw[x][2]), d = fp8x4_to_bf16x4(raw[x][3]);
+            lo[0] = a[0]; lo[1] = a[1]; lo[2] = b[0]; lo[3] = b[1];
+            hi[0] = cc[0]; hi[1] = cc[1]; hi[2] = d[0]; hi[3] = d[1];
+            *(u32x4_t*)(lds + T::off(R, 2 * c)) = lo;
+            *(u32x4_t*)(lds + T::off(R, 2 * c + 1)) = hi;
+        } else {
+            *(u32x4_t*)(lds + T::off(R, c)) = raw[x];
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+// fp16 LDS tile from raw V.  bf16 -> fp16 is exact for |v| in [2^-14, 65504]; smaller values
+// keep an absolute error below 2^-25, larger ones saturate.  FP8 codes convert exactly.
+template <int D, int KV>
+__device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds) {
+    using G = RawGeom<D, KV>;
+    using P = PfGeom<D, KV>;
+    using T = LdsTile<D>;
+#pragma unroll
+    for (int x = 0; x < P::NX; ++x) {
+        const int q = threadIdx.x + x * kPfThreads;
+        if (q >= P::CHUNKS) continue;
+        const int R = q / G::CPR, c = q % G::CPR;
+        if (KV == HS2_FP8_E4M3) {
+            u32x4_t lo, hi;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const f32x2_t a = fp8x2_to_f32<false>(raw[x][w]), b = fp8x2_to_f32<true>(raw[x][w]);
+                const uint32_t p0 = f16x2_bits(a[0], a[1]), p1 = f16x2_bits(b[0], b[1]);
+                if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; } else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
+            }
+            *(u32x4_t*)(lds + T::off(R, 2 * c)) = lo;
+            *(u32x4_t*)(lds + T::off(R, 2 * c + 1)) = hi;
+        } else {
+            u32x4_t o;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t u = raw[x][w];
+                o[w] = f16x2_bits(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
+            }
+            *(u32x4_t*)(lds + T::off(R, c)) = o;
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ f16x8_t lds_vt_operand_f16(const char* lds, int blk, int ks) {
+    return __builtin_bit_cast(f16x8_t, lds_vt_operand<D>(lds, blk, ks));
+}
+
+// Positions of the workgroup's query rows; returns the largest one (or -1).
+__device__ __forceinline__ int64_t pf_rows(const int32_t* q_pos, const int32_t* kv_len, int Tq, int64_t Nmax,
+                                           int b, int i0, int64_t* t_s) {
+    if (threadIdx.x < kPfWaves) {
+        const int i = i0 + threadIdx.x;
+        t_s[threadIdx.x] = i < Tq ? row_pos(q_pos, kv_len, b * Tq + i, Tq, Nmax) : -1;
+    }
+    __syncthreads();
+    int64_t tmax = -1;
+#pragma unroll
+    for (int w = 0; w < kPfWaves; ++w) tmax = t_s[w] > tmax ? t_s[w] : tmax;
+    return tmax;
+}
+
+// ---- pass 1 -------------------------------------------------------------------------------------
+template <int D, int KV>
+__global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a) {
+    constexpr int KS = D / 16, NB = D / 32;
+    constexpr int NX = PfGeom<D, KV>::NX;
+    constexpr int NST = 3;                       // tiles in flight in registers
+    __shared__ __attribute__((aligned(16))) char kt[2][LdsTile<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) char vt[2][LdsTile<D>::BYTES];
+    __shared__ float ks_s[2][kTileRows], vs_s[2][kTileRows];
+    __shared__ int64_t t_s[kPfWaves];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 31, hb = lane >> 5;
+    const int nqt = (a.Tq + kPfWaves - 1) / kPfWaves;
+    const int b = blockIdx.x / nqt, i0 = (blockIdx.x % nqt) * kPfWaves;
+    const int H = a.H;
+    const int64_t tmax = pf_rows(a.q_pos, a.kv_len, a.Tq, a.Nmax, b, i0, t_s);
+    const int64_t t = t_s[w];
+    const int r = b * a.Tq + (i0 + w < a.Tq ? i0 + w : a.Tq - 1);
+    const int64_t ntiles = (tmax + 1 + kTileRows - 1) / kTileRows;
+    const int64_t rowbase = (int64_t)b * a.Nmax;
+
+    bf16x8_t qop[KS];
+    {
+        const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * H + (n < H ? n : 0)) * D + hb * (D / 2));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qop[s] = n < H ? __builtin_bit_cast(bf16x8_t, qp[s]) : bf16x8_t{};
+    }
+    f32x16_t oacc[NB];
+#pragma unroll
+    for (int x = 0; x < NB; ++x) oacc[x] = f32x16_t{};
+    float m_run = kNegInf, l_run = 0.f;
+    const float sl2 = a.scale_log2;
+
+    if (ntiles > 0) {
+        const int64_t khi = tmax + 1;
+        u32x4_t rk[NST][NX], rv[NST][NX];
+        float rks[NST], rvs[NST];
+        auto load = [&](int st, int64_t tile) {
+            const int64_t tl = tile < ntiles ? tile : ntiles - 1;
+            pf_load<D, KV>(rk[st], a.k, rowbase, tl * kTileRows, khi);
+            pf_load<D, KV>(rv[st], a.v, rowbase, tl * kTileRows, khi);
+            if (KV == HS2_FP8_E4M3) {
+                const int64_t key = tl * kTileRows + (threadIdx.x & 31);
+                const int64_t kc = key < khi ? key : khi - 1;
+                rks[st] = a.k_scale[rowbase + kc];
+                rvs[st] = a.v_scale[rowbase + kc];
+            }
+        };
+        auto store = [&](int st, int buf) {
+            pf_store_k<D, KV>(rk[st], kt[buf]);
+            pf_store_v<D, KV>(rv[st], vt[buf]);
+            if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) { ks_s[buf][threadIdx.x] = rks[st]; vs_s[buf][threadIdx.x] = rvs[st]; }
+        };
+#pragma unroll
+        for (int u = 0; u < NST; ++u) load(u, u);
+        store(0, 0);
+        __syncthreads();
+        for (int64_t base = 0; base < ntiles; base += NST) {
+#pragma unroll
+            for (int u = 0; u < NST; ++u) {
+                const int64_t tile = base + u;
+                if (tile >= ntiles) break;
+                const int buf = (int)(tile & 1);
+                // refill the register stage of this tile with tile + NST, stage tile + 1 into LDS
+                // after the computation (its registers were filled NST - 1 tiles ago)
+                const int nst = (u + 1) % NST;
+                {
+                    // ---- compute tile from LDS buffer buf ----
+                    const int64_t k0 = tile * kTileRows;
+                    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand<D>(kt[buf], n, hb * (D / 16) + s),
+                                                                       qop[s], sacc, 0, 0, 0);
+                    float x[16];
+                    float mt = kNegInf;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int m = 8 * (i >> 2) + 4 * hb + (i & 3);
+                        float sc = sl2;
+                        if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][m];
+                        x[i] = (k0 + m <= t) ? sacc[i] * sc : kNegInf;
+                        mt = fmaxf(mt, x[i]);
+                    }
+                    mt = fmaxf(mt, __shfl_xor(mt, 32));
+                    const float mn = fmaxf(m_run, mt);
+                    const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
+                    const float mref = (mn == kNegInf) ? 0.f : mn;
+                    float ps = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        x[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+                        ps += x[i];
+                    }
+                    ps += __shfl_xor(ps, 32);
+                    l_run = l_run * alpha + ps;
+                    m_run = mn;
+                    if (KV == HS2_FP8_E4M3) {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) x[i] *= vs_s[buf][8 * (i >> 2) + 4 * hb + (i & 3)];
+                    }
+                    if (__ballot(alpha != 1.f)) {
+#pragma unroll
+                        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) oacc[blk][i] *= alpha;
+                    }
+                    f16x8_t p[2];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) { p[0][e] = (_Float16)x[e]; p[1][e] = (_Float16)x[8 + e]; }
+#pragma unroll
+                    for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                        for (int ks = 0; ks < 2; ++ks)
+                            oacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lds_vt_operand_f16<D>(vt[buf], blk, ks),
+                                                                               p[ks], oacc[blk], 0, 0, 0);
+                }
+                // stage tile + 1 (registers nst) into the other buffer, refill stage u with tile + NST
+                if (tile + 1 < ntiles) store(nst, buf ^ 1);
+                load(u, tile + NST);
+                __syncthreads();
+            }
+        }
+    }
+
+    // ---- finish: this workgroup saw every key of its rows ----
+    if (i0 + w < a.Tq) {
+        const float linv = l_run > 0.f ? 1.f / l_run : 0.f;
+        float* po = a.o + ((int64_t)r * H) * D;
+        if (n < H) {
+#pragma unroll
+            for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int dv = blk * 32 + 8 * g + 4 * hb;
+                    float4 v4;
+                    v4.x = oacc[blk][4 * g] * linv; v4.y = oacc[blk][4 * g + 1] * linv;
+                    v4.z = oacc[blk][4 * g + 2] * linv; v4.w = oacc[blk][4 * g + 3] * linv;
+                    *(float4*)(po + n * D + dv) = v4;
+                }
+            if (hb == 0 && a.lse) a.lse[(int64_t)r * H + n] = l_run > 0.f ? m_run + log2f(l_run) : kNegInf;
+        }
+    }
+}
+
+// ---- pass 2: selection scores ---------------------------------------------------------------------
+template <int D, int KV>
+__global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs a) {
+    constexpr int KS = D / 16;
+    constexpr int NX = PfGeom<D, KV>::NX;
+    constexpr int NST = 4;
+    __shared__ __attribute__((aligned(16))) char kt[2][LdsTile<D>::BYTES];
+    __shared__ float ks_s[2][kTileRows];
+    __shared__ uint32_t hist[kPfWaves][kHistBins];
+    __shared__ int64_t t_s[kPfWaves];
+
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int n = lane & 31, hb = lane >> 5;
+    const int nqt = (a.Tq + kPfWaves - 1) / kPfWaves;
+    const int b = blockIdx.x / nqt, i0 = (blockIdx.x % nqt) * kPfWaves;
+    const int H = a.H;
+    const int64_t tmax = pf_rows(a.q_pos, a.kv_len, a.Tq, a.Nmax, b, i0, t_s);
+    const int64_t t = t_s[w];
+    const bool live = i0 + w < a.Tq;
+    const int r = b * a.Tq + (live ? i0 + w : a.Tq - 1);
+    const int64_t C = cand_count(t, a.window);
+    const int64_t Cmax = cand_count(tmax, a.window);
+    const int64_t ntiles = (Cmax + kTileRows - 1) / kTileRows;
+    const int64_t rowbase = (int64_t)b * a.Nmax;
+    for (int x = threadIdx.x; x < kPfWaves * kHistBins; x += kPfThreads) (&hist[0][0])[x] = 0;
+
+    bf16x8_t qop[KS];
+    {
+        const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * H + (n < H ? n : 0)) * D + hb * (D / 2));
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qop[s] = n < H ? __builtin_bit_cast(bf16x8_t, qp[s]) : bf16x8_t{};
+    }
+    float nlse[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int h = 8 * (i >> 2) + 4 * hb + (i & 3);
+        nlse[i] = (h < H && C > 0) ? -a.lse[(int64_t)r * H + h] : kNegInf;
+    }
+    float* srow = a.scores + (int64_t)r * a.cstride;
+
+    if (ntiles > 0) {
+        u32x4_t rk[NST][NX];
+        float rks[NST];
+        auto load = [&](int st, int64_t tile) {
+            const int64_t tl = tile < ntiles ? tile : ntiles - 1;
+            pf_load<D, KV>(rk[st], a.k, rowbase, tl * kTileRows, Cmax);
+            if (KV == HS2_FP8_E4M3) {
+                const int64_t key = tl * kTileRows + (threadIdx.x & 31);
+                rks[st] = a.k_scale[rowbase + (key < Cmax ? key : Cmax - 1)];
+            }
+        };
+        auto store = [&](int st, int buf) {
+            pf_store_k<D, KV>(rk[st], kt[buf]);
+            if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) ks_s[buf][threadIdx.x] = rks[st];
+        };
+#pragma unroll
+        for (int u = 0; u < NST; ++u) load(u, u);
+        store(0, 0);
+        __syncthreads();
+        for (int64_t base = 0; base < ntiles; base += NST) {
+#pragma unroll
+            for (int u = 0; u < NST; ++u) {
+                const int64_t tile = base + u;
+                if (tile >= ntiles) break;
+                const int buf = (int)(tile & 1);
+                const int64_t k0 = tile * kTileRows;
+                if (k0 < C) {
+                    f32x16_t sacc = f32x16_t{};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s)
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], lds_row_operand<D>(kt[buf], n, hb * (D / 16) + s),
+                                                                       sacc, 0, 0, 0);
+                    float sc = a.scale_log2;
+                    if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][n];
+                    float acc = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(sacc[i] * sc + nlse[i]);
+                    acc += __shfl_xor(acc, 32);
+                    const int64_t j = k0 + n;
+                    if (hb == 0 && j < C) {
+                        srow[j] = acc;
+                        atomicAdd(&hist[w][__float_as_uint(acc) >> 21], 1u);
+                    }
+                }
+                if (tile + 1 < ntiles) store((u + 1) % NST, buf ^ 1);
+                load(u, tile + NST);
+                __syncthreads();
+            }
+        }
+    }
+    // this workgroup owns its rows' histograms entirely
+    __syncthreads();
+    if (a.rowhist) {
+        for (int x = threadIdx.x; x < kPfWaves * kHistBins; x += kPfThreads) {
+            const int ww = x / kHistBins;
+            if (i0 + ww < a.Tq) a.rowhist[((int64_t)b * a.Tq + i0 + ww) * kHistBins + (x % kHistBins)] = hist[ww][x % kHistBins];
+        }
+    }
+}
+
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s) {
+    ProfScope ps("full_attn_prefill", s);
+    const int nqt = (a.Tq + kPfWaves - 1) / kPfWaves;
+    dim3 grid(a.B * nqt);
+    if (a.kv_dtype == HS2_FP8_E4M3) {
+        if (a.d == 128) attn_prefill_kernel<128, HS2_FP8_E4M3><<<grid, kPfThreads, 0, s>>>(a);
+        else attn_prefill_kernel<64, HS2_FP8_E4M3><<<grid, kPfThreads, 0, s>>>(a);
+    } else {
+        if (a.d == 128) attn_prefill_kernel<128, HS2_BF16><<<grid, kPfThreads, 0, s>>>(a);
+        else attn_prefill_kernel<64, HS2_BF16><<<grid, kPfThreads, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t s) {
+    ProfScope ps("score_prefill", s);
+    const int nqt = (a.Tq + kPfWaves - 1) / kPfWaves;
+    dim3 grid(a.B * nqt);
+    if (a.kv_dtype == HS2_FP8_E4M3) {
+        if (a.d == 128) score_prefill_kernel<128, HS2_FP8_E4M3><<<grid, kPfThreads, 0, s>>>(a);
+        else score_prefill_kernel<64, HS2_FP8_E4M3><<<grid, kPfThreads, 0, s>>>(a);
+    } else {
+        if (a.d == 128) score_prefill_kernel<128, HS2_BF16><<<grid, kPfThreads, 0, s>>>(a);
+        else score_prefill_kernel<64, HS2_BF16><<<grid, kPfThreads, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace hs2

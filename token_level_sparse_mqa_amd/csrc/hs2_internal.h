@@ -75,6 +75,8 @@ hipError_t launch_bridge_generic(const BridgeArgs& a, hipStream_t s);
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_rows_mfma(const ScoreArgs& a, hipStream_t s);
+hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t launch_score_prefill(const ScoreArgs& a, hipStream_t s);
 
 // Measurement hook: brackets a launch with events on `s` while profiling is enabled.
 struct ProfScope {
