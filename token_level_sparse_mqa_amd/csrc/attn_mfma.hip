@@ -80,8 +80,8 @@ template <int D, int KV>
 __device__ __forceinline__ uint32_t stage_row_tile(const RowTile<D, KV>& T, RowWaveLds<D>& W) {
     const int lane = threadIdx.x & 63;
     const uint32_t valid = (uint32_t)__ballot(T.kid >= 0);      // bit m: row m holds a key
-    store_lds_tile<D, KV>(T.k, W.k, [](int) { return true; });
-    store_lds_tile<D, KV>(T.v, W.v, [&](int R) { return (valid >> R) & 1u; });
+    store_lds_tile<D, KV, false>(T.k, W.k, [](int) { return true; });
+    store_lds_tile<D, KV, true>(T.v, W.v, [&](int R) { return (valid >> R) & 1u; });
     if (KV == HS2_FP8_E4M3 && lane < 32) { W.ks[lane] = T.ks; W.vs[lane] = T.vs; }
     return valid;
 }
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(ScoreArgs a) {
                 load(kb[(u + NBUF - 1) % NBUF], ksb[(u + NBUF - 1) % NBUF], it + NBUF - 1);
                 if (it < ntw) {
                     const int64_t tile = w + (int64_t)kRowWaves * it;
-                    store_lds_tile<D, KV>(kb[u], klds, [](int) { return true; });
+                    store_lds_tile<D, KV, false>(kb[u], klds, [](int) { return true; });
                     wave_lds_fence();
                     f32x16_t sacc = f32x16_t{};
 #pragma unroll

@@ -30,19 +30,39 @@ struct PfGeom {
     static constexpr int NX = (CHUNKS + kPfThreads - 1) / kPfThreads;    // loads per thread
 };
 
+// Per-thread part of the cooperative tile loads: load x of a thread reads 16-byte chunk c of tile
+// row R, at byte offset (k0 + R) * RB + 16 c from the sequence's first cache row.  Offsets are
+// 32-bit (the host keeps Nmax * row bytes below 2^31).
 template <int D, int KV>
-__device__ __forceinline__ void pf_load(u32x4_t* raw, const void* base, int64_t rowbase, int64_t k0, int64_t khi) {
+struct PfLoader {
     using G = RawGeom<D, KV>;
     using P = PfGeom<D, KV>;
+    uint32_t off[P::NX];      // R * RB + 16 c
+    int R[P::NX];
+    __device__ __forceinline__ PfLoader() {
 #pragma unroll
-    for (int x = 0; x < P::NX; ++x) {
-        int q = threadIdx.x + x * kPfThreads;
-        q = q < P::CHUNKS ? q : P::CHUNKS - 1;
-        const int R = q / G::CPR, c = q % G::CPR;
-        const int64_t key = k0 + R < khi ? k0 + R : khi - 1;
-        raw[x] = *(const u32x4_t*)((const char*)base + (rowbase + key) * G::RB + 16 * c);
+        for (int x = 0; x < P::NX; ++x) {
+            int q = threadIdx.x + x * kPfThreads;
+            q = q < P::CHUNKS ? q : P::CHUNKS - 1;
+            R[x] = q / G::CPR;
+            off[x] = (uint32_t)(R[x] * G::RB + 16 * (q % G::CPR));
+        }
     }
-}
+    // rows k0 .. k0+31; rows at or past khi read row khi - 1 instead
+    __device__ __forceinline__ void load(u32x4_t* raw, const char* seq, int64_t k0, int64_t khi) const {
+        if (k0 + kTileRows <= khi) {
+            const uint32_t base = (uint32_t)k0 * G::RB;
+#pragma unroll
+            for (int x = 0; x < P::NX; ++x) raw[x] = *(const u32x4_t*)(seq + (base + off[x]));
+        } else {
+#pragma unroll
+            for (int x = 0; x < P::NX; ++x) {
+                const int64_t key = k0 + R[x] < khi ? k0 + R[x] : khi - 1;
+                raw[x] = *(const u32x4_t*)(seq + ((uint32_t)key * G::RB + (off[x] - (uint32_t)R[x] * G::RB)));
+            }
+        }
+    }
+};
 
 // bf16 LDS tile from raw K (FP8 codes converted exactly).
 template <int D, int KV>
@@ -93,8 +113,8 @@ __device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds) {
                 const uint32_t p0 = f16x2_bits(a[0], a[1]), p1 = f16x2_bits(b[0], b[1]);
                 if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; } else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
             }
-            *(u32x4_t*)(lds + T::off(R, 2 * c)) = lo;
-            *(u32x4_t*)(lds + T::off(R, 2 * c + 1)) = hi;
+            *(u32x4_t*)(lds + T::voff(R, 2 * c)) = lo;
+            *(u32x4_t*)(lds + T::voff(R, 2 * c + 1)) = hi;
         } else {
             u32x4_t o;
 #pragma unroll
@@ -102,7 +122,7 @@ __device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds) {
                 const uint32_t u = raw[x][w];
                 o[w] = f16x2_bits(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
             }
-            *(u32x4_t*)(lds + T::off(R, c)) = o;
+            *(u32x4_t*)(lds + T::voff(R, c)) = o;
         }
     }
 }
@@ -162,12 +182,15 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
 
     if (ntiles > 0) {
         const int64_t khi = tmax + 1;
+        const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
+        const char* vseq = (const char*)a.v + rowbase * RawGeom<D, KV>::RB;
+        const PfLoader<D, KV> ld;
         u32x4_t rk[NST][NX], rv[NST][NX];
         float rks[NST], rvs[NST];
         auto load = [&](int st, int64_t tile) {
             const int64_t tl = tile < ntiles ? tile : ntiles - 1;
-            pf_load<D, KV>(rk[st], a.k, rowbase, tl * kTileRows, khi);
-            pf_load<D, KV>(rv[st], a.v, rowbase, tl * kTileRows, khi);
+            ld.load(rk[st], kseq, tl * kTileRows, khi);
+            ld.load(rv[st], vseq, tl * kTileRows, khi);
             if (KV == HS2_FP8_E4M3) {
                 const int64_t key = tl * kTileRows + (threadIdx.x & 31);
                 const int64_t kc = key < khi ? key : khi - 1;
@@ -190,35 +213,41 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                 const int64_t tile = base + u;
                 if (tile >= ntiles) break;
                 const int buf = (int)(tile & 1);
-                // refill the register stage of this tile with tile + NST, stage tile + 1 into LDS
-                // after the computation (its registers were filled NST - 1 tiles ago)
-                const int nst = (u + 1) % NST;
-                {
-                    // ---- compute tile from LDS buffer buf ----
-                    const int64_t k0 = tile * kTileRows;
+                const int64_t k0 = tile * kTileRows;
+                if (k0 <= t) {
                     f32x16_t sacc = f32x16_t{};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
                         sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand<D>(kt[buf], n, hb * (D / 16) + s),
                                                                        qop[s], sacc, 0, 0, 0);
+                    // logits x = s * sc (sc > 0); keys past t are masked in the tile holding t
                     float x[16];
-                    float mt = kNegInf;
+                    if (KV == HS2_FP8_E4M3) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int m = 8 * (i >> 2) + 4 * hb + (i & 3);
-                        float sc = sl2;
-                        if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][m];
-                        x[i] = (k0 + m <= t) ? sacc[i] * sc : kNegInf;
-                        mt = fmaxf(mt, x[i]);
+                        for (int i = 0; i < 16; ++i) x[i] = sacc[i] * (sl2 * ks_s[buf][8 * (i >> 2) + 4 * hb + (i & 3)]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) x[i] = sacc[i];
                     }
+                    if (k0 + kTileRows - 1 > t) {
+                        const int lim = (int)(t - k0);
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            if (8 * (i >> 2) + 4 * hb + (i & 3) > lim) x[i] = kNegInf;
+                    }
+                    float mt = x[0];
+#pragma unroll
+                    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
                     mt = fmaxf(mt, __shfl_xor(mt, 32));
-                    const float mn = fmaxf(m_run, mt);
+                    // bf16 path: x is still unscaled, scale the maximum (sc > 0 keeps the order)
+                    const float scl = KV == HS2_FP8_E4M3 ? 1.f : sl2;
+                    const float mn = fmaxf(m_run, mt * scl);
                     const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
                     const float mref = (mn == kNegInf) ? 0.f : mn;
                     float ps = 0.f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        x[i] = __builtin_amdgcn_exp2f(x[i] - mref);
+                        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scl, -mref));
                         ps += x[i];
                     }
                     ps += __shfl_xor(ps, 32);
@@ -244,8 +273,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                             oacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lds_vt_operand_f16<D>(vt[buf], blk, ks),
                                                                                p[ks], oacc[blk], 0, 0, 0);
                 }
-                // stage tile + 1 (registers nst) into the other buffer, refill stage u with tile + NST
-                if (tile + 1 < ntiles) store(nst, buf ^ 1);
+                // stage tile + 1 (registers (u+1) % NST) into the other buffer, refill stage u
+                if (tile + 1 < ntiles) store((u + 1) % NST, buf ^ 1);
                 load(u, tile + NST);
                 __syncthreads();
             }
@@ -313,11 +342,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
     float* srow = a.scores + (int64_t)r * a.cstride;
 
     if (ntiles > 0) {
+        const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
+        const PfLoader<D, KV> ld;
         u32x4_t rk[NST][NX];
         float rks[NST];
         auto load = [&](int st, int64_t tile) {
             const int64_t tl = tile < ntiles ? tile : ntiles - 1;
-            pf_load<D, KV>(rk[st], a.k, rowbase, tl * kTileRows, Cmax);
+            ld.load(rk[st], kseq, tl * kTileRows, Cmax);
             if (KV == HS2_FP8_E4M3) {
                 const int64_t key = tl * kTileRows + (threadIdx.x & 31);
                 rks[st] = a.k_scale[rowbase + (key < Cmax ? key : Cmax - 1)];
@@ -348,7 +379,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
                     if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][n];
                     float acc = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(sacc[i] * sc + nlse[i]);
+                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sc, nlse[i]));
                     acc += __shfl_xor(acc, 32);
                     const int64_t j = k0 + n;
                     if (hb == 0 && j < C) {

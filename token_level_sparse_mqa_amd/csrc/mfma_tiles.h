@@ -59,7 +59,10 @@ __device__ __forceinline__ void wave_lds_fence() {
     __builtin_amdgcn_wave_barrier();
 }
 
-// ---- the LDS tile: 32 rows of D bf16 ----------------------------------------------------------
+// ---- the LDS tile: 32 rows of D 16-bit values ---------------------------------------------------
+// K tiles are read as 16-byte row chunks by 32 lanes at a time (chunk XOR row spreads them over
+// the banks); V tiles are read transposed, 4 consecutive rows x 2 adjacent chunks per 16-lane
+// group (chunk XOR 2 * (row mod 8) gives those 8 pieces 8 different bank groups).
 template <int D>
 struct LdsTile {
     static constexpr int RB = D * 2;          // bytes per row
@@ -67,6 +70,9 @@ struct LdsTile {
     static constexpr int BYTES = kTileRows * RB;
     __device__ static __forceinline__ int off(int row, int chunk) {
         return row * RB + ((chunk ^ (row & (CPR - 1))) << 4);
+    }
+    __device__ static __forceinline__ int voff(int row, int chunk) {
+        return row * RB + ((chunk ^ ((row << 1) & (CPR - 2))) << 4);
     }
 };
 
@@ -95,11 +101,13 @@ __device__ __forceinline__ void load_raw_tile(u32x4_t* raw, const void* base, Ro
     }
 }
 
-// Store a raw tile into the LDS tile as bf16 (rows with keep(R) == false become zero).
-template <int D, int KV, class KeepFn>
+// Store a raw tile into the LDS tile as bf16 (rows with keep(R) == false become zero), in the
+// K layout or (VT = true) the V layout.
+template <int D, int KV, bool VT, class KeepFn>
 __device__ __forceinline__ void store_lds_tile(const u32x4_t* raw, char* lds, KeepFn keep) {
     using G = RawGeom<D, KV>;
     using T = LdsTile<D>;
+    auto off = [](int row, int chunk) { return VT ? T::voff(row, chunk) : T::off(row, chunk); };
     const int lane = threadIdx.x & 63;
     const int c = lane % G::CPR;
 #pragma unroll
@@ -113,12 +121,12 @@ __device__ __forceinline__ void store_lds_tile(const u32x4_t* raw, char* lds, Ke
             const u32x2_t cc = fp8x4_to_bf16x4(raw[x][2] & msk), d = fp8x4_to_bf16x4(raw[x][3] & msk);
             lo[0] = a[0]; lo[1] = a[1]; lo[2] = b[0]; lo[3] = b[1];
             hi[0] = cc[0]; hi[1] = cc[1]; hi[2] = d[0]; hi[3] = d[1];
-            *(u32x4_t*)(lds + T::off(R, 2 * c)) = lo;
-            *(u32x4_t*)(lds + T::off(R, 2 * c + 1)) = hi;
+            *(u32x4_t*)(lds + off(R, 2 * c)) = lo;
+            *(u32x4_t*)(lds + off(R, 2 * c + 1)) = hi;
         } else {
             u32x4_t v = raw[x];
             v[0] &= msk; v[1] &= msk; v[2] &= msk; v[3] &= msk;
-            *(u32x4_t*)(lds + T::off(R, c)) = v;
+            *(u32x4_t*)(lds + off(R, c)) = v;
         }
     }
 }
@@ -144,7 +152,7 @@ __device__ __forceinline__ bf16x8_t lds_vt_operand(const char* lds, int blk, int
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int key = 16 * ks + 8 * h + 4 * hb + (q >> 2);
-        const char* p = lds + LdsTile<D>::off(key, dv >> 3) + (dv & 7) * 2;
+        const char* p = lds + LdsTile<D>::voff(key, dv >> 3) + (dv & 7) * 2;
         const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
         const u32x2_t tu = __builtin_bit_cast(u32x2_t, t);
         r[2 * h] = tu[0];
