@@ -218,7 +218,7 @@ hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D, const void* w
     if (!hidden || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARG, "null pointer");
     BridgeArgs a{(const uint16_t*)hidden, T, D, (const uint16_t*)w_k, (const uint16_t*)w_v, d,
                  (uint16_t*)k_out, (uint16_t*)v_out, out_row_stride};
-    hipError_t e = launch_bridge_generic(a, stream);
+    hipError_t e = launch_bridge_mfma(a, stream);
     if (e != hipSuccess) return hip_fail(e, "kv_bridge launch");
     return HS2_OK;
 }
