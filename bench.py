@@ -161,20 +161,29 @@ def run_gpu(cfg, steps, warmup, profile=True):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(nsteps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(nsteps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nsteps, time.perf_counter() - w0
+
+    # the step time comes from a region without per-kernel events (an event record between two
+    # kernels serialises them); the per-kernel durations from a second region of the same length
     log(f"[bench] timing {steps} steps")
-    hs2.profile_enable(profile)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms = e0.elapsed_time(e1) / steps
-    kernels = hs2.profile_read() if profile else {}
-    hs2.profile_enable(False)
+    ms, wall = timed(steps)
+    kernels = {}
+    if profile:
+        log(f"[bench] per-kernel event timing, {steps} steps")
+        hs2.profile_enable(True)
+        timed(steps)
+        kernels = hs2.profile_read()
+        hs2.profile_enable(False)
     return {"ms_per_step": ms, "wall_s": wall, "rows": R, "kernels": kernels, "wl": wl}
 
 

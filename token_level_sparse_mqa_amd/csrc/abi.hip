@@ -51,7 +51,6 @@ struct SelectPlan {
     int score_nsplit; int64_t score_chunk;
     int nseg;
     size_t off_part, off_lse, off_scores, off_hist, off_cnt, off_sure, off_cand, total;
-    size_t zero_off, zero_words;       // rowhist + counters, cleared at the start of a call
 };
 
 // Split a key range of n entries over workgroups: at least `min_chunk` entries each (a multiple
@@ -89,8 +88,6 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
     p.off_lse = off;    off = align_up(off + (size_t)p.R * H * 4);
     p.off_hist = off;   off = off + (size_t)p.R * kHistBins * 4;
     p.off_cnt = off;    off = align_up(off + (size_t)p.R * 4 * 4);
-    p.zero_off = p.off_hist;
-    p.zero_words = (p.off_cnt + (size_t)p.R * 16 - p.off_hist) / 4;
     p.off_sure = off;   off = align_up(off + (size_t)p.R * k_global * 4);
     p.off_cand = off;   off = align_up(off + (size_t)p.R * kSelCap * 8);
     p.off_scores = off; off = align_up(off + (size_t)p.R * Nmax * 4);
@@ -254,9 +251,7 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     uint32_t* counters = (uint32_t*)(ws + p.off_cnt);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
 
-    hipError_t e = launch_zero_u32((uint32_t*)(ws + p.zero_off), p.zero_words, stream);
-    if (e != hipSuccess) return hip_fail(e, "workspace clear");
-
+    hipError_t e;
     AttnArgs aa{};
     aa.q = q; aa.q_dtype = q_dtype; aa.k = k; aa.v = v; aa.kv_dtype = kv_dtype;
     aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = q_pos; aa.kv_len = kv_len;
@@ -264,6 +259,8 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     aa.scale_log2 = scale_log2; aa.nsplit = p.nsplit; aa.chunk = p.chunk;
     aa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
     aa.o = o; aa.lse = lse;
+    aa.waves = 4;
+    aa.zero_hist = rowhist; aa.zero_cnt = counters;     // cleared by the attention pass
     if (p.path == PATH_GENERIC) {
         e = launch_attn_generic(aa, "full_attn_generic", stream);
         if (e != hipSuccess) return hip_fail(e, "attention launch");
@@ -323,6 +320,7 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
     aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = nullptr; aa.kv_len = kv_len;
     aa.list = idx; aa.S = S; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
     aa.scale_log2 = sm_scale * 1.4426950408889634f;
+    aa.waves = 4;
     if (split) {
         sparse_plan(R, S, q_dtype, &aa.nsplit, &aa.chunk);
     } else {

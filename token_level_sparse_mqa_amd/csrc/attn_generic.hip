@@ -39,6 +39,11 @@ __global__ __launch_bounds__(kGenThreads) void attn_generic_kernel(AttnArgs a) {
         e1 = e0 + a.chunk < t + 1 ? e0 + a.chunk : t + 1;
     }
 
+    // this row's selection workspace is cleared here, before the score pass accumulates into it
+    if (a.zero_hist && split == 0) {
+        for (int x = tid; x < kHistBins; x += kGenThreads) a.zero_hist[(int64_t)r * kHistBins + x] = 0;
+        if (tid < 4) a.zero_cnt[(int64_t)r * 4 + tid] = 0;
+    }
     for (int x = tid; x < 32 * D; x += kGenThreads) {
         const int h = x / D, c = x % D;
         qs[h][c] = h < H ? load_elem(a.q, a.q_dtype, ((int64_t)r * H + h) * D + c) * a.scale_log2 : 0.f;

@@ -160,15 +160,17 @@ __device__ __forceinline__ void row_tile_step(const RowWaveLds<D>& W, uint32_t v
 }
 
 // ---- the attention kernel -------------------------------------------------------------------------
-// Two workgroups (eight waves) per CU: while one wave waits on LDS or MFMA results the other
-// computes, and each wave keeps its next tile in flight in registers.
-template <int D, int KV>
-__global__ __launch_bounds__(256, 2)
+// NW = 4: two workgroups (eight waves) per CU, so while one wave waits on LDS or MFMA results
+// the other computes; each wave keeps its next tile in flight in registers.  NW = 8: one
+// workgroup per row with no split (few rows, e.g. decode sparse layers), no combine pass.
+template <int D, int KV, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
 void attn_rows_mfma_kernel(AttnArgs a) {
+    constexpr int NT = NW * 64;
     constexpr int NB = D / 32;
-    __shared__ __attribute__((aligned(16))) RowWaveLds<D> wl_s[kRowWaves];
+    __shared__ __attribute__((aligned(16))) RowWaveLds<D> wl_s[NW];
     __shared__ __attribute__((aligned(16))) char q_s[LdsTile<D>::BYTES];
-    __shared__ float ml_s[kRowWaves][32][2];
+    __shared__ float ml_s[NW][32][2];
     __shared__ int32_t ids_s[kRowListMax];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -186,16 +188,21 @@ void attn_rows_mfma_kernel(AttnArgs a) {
         e1 = e0 + a.chunk < t + 1 ? e0 + a.chunk : t + 1;
     }
     const int64_t ntiles = e1 > e0 ? (e1 - e0 + 31) / 32 : 0;
+    // this row's selection workspace is cleared here, before the score pass accumulates into it
+    if (a.zero_hist && split == 0) {
+        for (int x = threadIdx.x; x < kHistBins; x += NT) a.zero_hist[(int64_t)r * kHistBins + x] = 0;
+        if (threadIdx.x < 4) a.zero_cnt[(int64_t)r * 4 + threadIdx.x] = 0;
+    }
     const int32_t* ids = nullptr;
     if (a.list) {
-        for (int64_t x = threadIdx.x; x < e1 - e0; x += 256) ids_s[x] = a.list[(int64_t)r * a.S + e0 + x];
+        for (int64_t x = threadIdx.x; x < e1 - e0; x += NT) ids_s[x] = a.list[(int64_t)r * a.S + e0 + x];
         ids = ids_s;
     }
     // Q (heads padded to 32 with zeros) as an LDS tile: the Q^T operand of every MFMA step
     {
         const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * H * D);
         constexpr int CPR = LdsTile<D>::CPR;
-        for (int x = threadIdx.x; x < 32 * CPR; x += 256) {
+        for (int x = threadIdx.x; x < 32 * CPR; x += NT) {
             const int h = x / CPR, c = x % CPR;
             *(u32x4_t*)(q_s + LdsTile<D>::off(h, c)) = h < H ? qp[h * CPR + c] : u32x4_t{0, 0, 0, 0};
         }
@@ -212,9 +219,9 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     // one tile in registers in flight while the previous one is computed from LDS; the refill
     // past the wave's last tile re-loads that tile (a cache hit), keeping the loads unconditional
     RowTile<D, KV> T;
-    const int64_t ntw = ntiles > w ? (ntiles - w + kRowWaves - 1) / kRowWaves : 0;   // tiles of this wave
+    const int64_t ntw = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles of this wave
     if (ntw > 0) {
-        auto tile_e = [&](int64_t it) { return e0 + 32 * (w + (int64_t)kRowWaves * (it < ntw ? it : ntw - 1)); };
+        auto tile_e = [&](int64_t it) { return e0 + 32 * (w + (int64_t)NW * (it < ntw ? it : ntw - 1)); };
         load_row_tile<D, KV>(T, a, rowbase, L, e0, e1, tile_e(0), ids);
         for (int64_t it = 0; it < ntw; ++it) {
             const uint32_t valid = stage_row_tile<D, KV>(T, W);
@@ -230,15 +237,15 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     __syncthreads();
     float M = kNegInf;
 #pragma unroll
-    for (int ww = 0; ww < kRowWaves; ++ww) M = fmaxf(M, ml_s[ww][n][0]);
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml_s[ww][n][0]);
     float myscale = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kRowWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
         const float mw = ml_s[ww][n][0];
         if (ww == w) myscale = (mw == kNegInf) ? 0.f : exp2f(mw - M);
     }
     float* obuf = (float*)&wl_s[0];     // [32 heads][D] fp32, reusing the tile space
-    for (int ww = 0; ww < kRowWaves; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
         if (w == ww) {
 #pragma unroll
             for (int blk = 0; blk < NB; ++blk)
@@ -251,13 +258,13 @@ void attn_rows_mfma_kernel(AttnArgs a) {
         }
         __syncthreads();
     }
-    for (int x = threadIdx.x; x < H * D; x += 256) {
+    for (int x = threadIdx.x; x < H * D; x += NT) {
         const int h = x / D, dv = x % D;
         float Mh = kNegInf, Lh = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < kRowWaves; ++ww) Mh = fmaxf(Mh, ml_s[ww][h][0]);
+        for (int ww = 0; ww < NW; ++ww) Mh = fmaxf(Mh, ml_s[ww][h][0]);
 #pragma unroll
-        for (int ww = 0; ww < kRowWaves; ++ww) {
+        for (int ww = 0; ww < NW; ++ww) {
             const float mw = ml_s[ww][h][0];
             Lh += mw == kNegInf ? 0.f : ml_s[ww][h][1] * exp2f(mw - Mh);
         }
@@ -430,16 +437,22 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(ScoreArgs a) {
 }
 
 // ---- launchers -------------------------------------------------------------------------------------
+template <int NW>
+static void launch_rows_nw(const AttnArgs& a, dim3 grid, hipStream_t s) {
+    if (a.kv_dtype == HS2_FP8_E4M3) {
+        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_FP8_E4M3, NW><<<grid, NW * 64, 0, s>>>(a);
+        else attn_rows_mfma_kernel<64, HS2_FP8_E4M3, NW><<<grid, NW * 64, 0, s>>>(a);
+    } else {
+        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_BF16, NW><<<grid, NW * 64, 0, s>>>(a);
+        else attn_rows_mfma_kernel<64, HS2_BF16, NW><<<grid, NW * 64, 0, s>>>(a);
+    }
+}
+
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s) {
     ProfScope ps(name, s);
     dim3 grid(a.B * a.Tq, a.nsplit);
-    if (a.kv_dtype == HS2_FP8_E4M3) {
-        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_FP8_E4M3><<<grid, 256, 0, s>>>(a);
-        else attn_rows_mfma_kernel<64, HS2_FP8_E4M3><<<grid, 256, 0, s>>>(a);
-    } else {
-        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_BF16><<<grid, 256, 0, s>>>(a);
-        else attn_rows_mfma_kernel<64, HS2_BF16><<<grid, 256, 0, s>>>(a);
-    }
+    if (a.waves == 8) launch_rows_nw<8>(a, grid, s);
+    else launch_rows_nw<4>(a, grid, s);
     return hipGetLastError();
 }
 

@@ -167,6 +167,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     const int r = b * a.Tq + (i0 + w < a.Tq ? i0 + w : a.Tq - 1);
     const int64_t ntiles = (tmax + 1 + kTileRows - 1) / kTileRows;
     const int64_t rowbase = (int64_t)b * a.Nmax;
+    // the selection counters of these rows are cleared here (the score pass writes the whole
+    // radix histogram of each row itself)
+    if (a.zero_cnt && threadIdx.x < 4 * kPfWaves && i0 + (int)threadIdx.x / 4 < a.Tq)
+        a.zero_cnt[((int64_t)b * a.Tq + i0) * 4 + threadIdx.x] = 0;
 
     bf16x8_t qop[KS];
     {

@@ -32,6 +32,9 @@ struct AttnArgs {
     float* part;                         // [R, nsplit, H, d + 2]: o, m, l of each split
     float* o;                            // [R, H, d]
     float* lse;                          // [R, H] base-2 log-sum-exp (nullptr: not needed)
+    int waves;                           // waves per workgroup of the row kernel (4 or 8)
+    uint32_t* zero_hist;                 // [R, kHistBins] to clear (nullptr: none)
+    uint32_t* zero_cnt;                  // [R, 4] to clear
 };
 
 struct ScoreArgs {
@@ -69,7 +72,6 @@ struct BridgeArgs {
 hipError_t launch_attn_generic(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_generic(const ScoreArgs& a, hipStream_t s);
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s);
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s);
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s);

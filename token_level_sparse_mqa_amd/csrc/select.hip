@@ -334,19 +334,6 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
     }
 }
 
-__global__ void zero_u32_kernel(uint32_t* p, size_t n) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0;
-}
-
-hipError_t launch_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
-    ProfScope ps("zero", s);
-    size_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks == 0) return hipSuccess;
-    zero_u32_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, n);
-    return hipGetLastError();
-}
-
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
     dim3 grid(a.R, a.nseg);
     if (!hist_done) {
