@@ -258,8 +258,8 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     aa.list = nullptr; aa.S = 0; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
     aa.scale_log2 = scale_log2; aa.nsplit = p.nsplit; aa.chunk = p.chunk;
     aa.part = p.nsplit > 1 ? (float*)(ws + p.off_part) : nullptr;
+    aa.part_ml = aa.part ? aa.part + p.R * p.nsplit * H * d : nullptr;   // MFMA layout
     aa.o = o; aa.lse = lse;
-    aa.waves = 4;
     aa.zero_hist = rowhist; aa.zero_cnt = counters;     // cleared by the attention pass
     if (p.path == PATH_GENERIC) {
         e = launch_attn_generic(aa, "full_attn_generic", stream);
@@ -320,7 +320,6 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
     aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = nullptr; aa.kv_len = kv_len;
     aa.list = idx; aa.S = S; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
     aa.scale_log2 = sm_scale * 1.4426950408889634f;
-    aa.waves = 4;
     if (split) {
         sparse_plan(R, S, q_dtype, &aa.nsplit, &aa.chunk);
     } else {
@@ -331,6 +330,7 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
     // take the generic kernel
     const bool mfma = q_dtype != HS2_F32 && aa.chunk <= 1280;
     aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
+    aa.part_ml = aa.part ? aa.part + R * aa.nsplit * H * d : nullptr;   // MFMA layout
     aa.o = o; aa.lse = nullptr;
     hipError_t e;
     if (!mfma) {

@@ -160,17 +160,18 @@ __device__ __forceinline__ void row_tile_step(const RowWaveLds<D>& W, uint32_t v
 }
 
 // ---- the attention kernel -------------------------------------------------------------------------
-// NW = 4: two workgroups (eight waves) per CU, so while one wave waits on LDS or MFMA results
-// the other computes; each wave keeps its next tile in flight in registers.  NW = 8: one
-// workgroup per row with no split (few rows, e.g. decode sparse layers), no combine pass.
-template <int D, int KV, int NW>
-__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1)
+// Two workgroups (eight waves) per CU, so while one wave waits on LDS or MFMA results the other
+// computes; each wave keeps its next tile in flight in registers.
+template <int D, int KV>
+__global__ __launch_bounds__(kRowWaves * 64, 2)
 void attn_rows_mfma_kernel(AttnArgs a) {
+    constexpr int NW = kRowWaves;
     constexpr int NT = NW * 64;
     constexpr int NB = D / 32;
     __shared__ __attribute__((aligned(16))) RowWaveLds<D> wl_s[NW];
     __shared__ __attribute__((aligned(16))) char q_s[LdsTile<D>::BYTES];
     __shared__ float ml_s[NW][32][2];
+    __shared__ float mlf_s[32][2];
     __shared__ int32_t ids_s[kRowListMax];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -216,67 +217,88 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     const float sl2 = a.scale_log2;
     const int64_t rowbase = (int64_t)b * a.Nmax;
 
-    // one tile in registers in flight while the previous one is computed from LDS; the refill
-    // past the wave's last tile re-loads that tile (a cache hit), keeping the loads unconditional
+    // one tile in registers in flight while the previous one is computed from LDS; the loop
+    // loads unconditionally and the wave's last tile is peeled off, so no load is issued past it
     RowTile<D, KV> T;
     const int64_t ntw = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles of this wave
     if (ntw > 0) {
-        auto tile_e = [&](int64_t it) { return e0 + 32 * (w + (int64_t)NW * (it < ntw ? it : ntw - 1)); };
+        auto tile_e = [&](int64_t it) { return e0 + 32 * (w + (int64_t)NW * it); };
         load_row_tile<D, KV>(T, a, rowbase, L, e0, e1, tile_e(0), ids);
-        for (int64_t it = 0; it < ntw; ++it) {
+        for (int64_t it = 0; it + 1 < ntw; ++it) {
             const uint32_t valid = stage_row_tile<D, KV>(T, W);
             load_row_tile<D, KV>(T, a, rowbase, L, e0, e1, tile_e(it + 1), ids);
             wave_lds_fence();
             row_tile_step<D, KV>(W, valid, q_s, oacc, m_run, l_run, sl2);
             wave_lds_fence();
         }
+        const uint32_t valid = stage_row_tile<D, KV>(T, W);
+        wave_lds_fence();
+        row_tile_step<D, KV>(W, valid, q_s, oacc, m_run, l_run, sl2);
+        wave_lds_fence();
     }
 
     // ---- merge the waves of the workgroup ----
+    // every lane combines the (m, l) of its head n over the waves and keeps its own wave's scale
     if (lane < 32) { ml_s[w][n][0] = m_run; ml_s[w][n][1] = l_run; }
     __syncthreads();
     float M = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, ml_s[ww][n][0]);
-    float myscale = 0.f;
+    float Lsum = 0.f, myscale = 0.f;
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
         const float mw = ml_s[ww][n][0];
-        if (ww == w) myscale = (mw == kNegInf) ? 0.f : exp2f(mw - M);
+        const float sc = mw == kNegInf ? 0.f : exp2f(mw - M);
+        Lsum += ml_s[ww][n][1] * sc;
+        if (ww == w) myscale = sc;
     }
-    float* obuf = (float*)&wl_s[0];     // [32 heads][D] fp32, reusing the tile space
-    for (int ww = 0; ww < NW; ++ww) {
-        if (w == ww) {
+    if (w == 0 && lane < 32) { mlf_s[n][0] = M; mlf_s[n][1] = Lsum; }
+    // each wave stores its scaled O^T in its own (now idle) tile space as float4s of four
+    // consecutive dv: float4 q = dv / 4 of head n sits at n * QN + (q ^ (n mod QN)), which keeps
+    // these stores and the cross-wave loads below free of bank conflicts
+    constexpr int QN = D / 4;
+    {
+        float4* ob = (float4*)&wl_s[w];
 #pragma unroll
-            for (int blk = 0; blk < NB; ++blk)
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int dv = blk * 32 + 8 * (i >> 2) + 4 * hb + (i & 3);
-                    const float v = oacc[blk][i] * myscale;
-                    obuf[n * D + dv] = ww == 0 ? v : obuf[n * D + dv] + v;
-                }
-        }
-        __syncthreads();
+            for (int g = 0; g < 4; ++g) {
+                const int q = 8 * blk + 2 * g + hb;          // dv = 32 blk + 8 g + 4 hb + j
+                ob[n * QN + (q ^ (n & (QN - 1)))] =
+                    make_float4(oacc[blk][4 * g] * myscale, oacc[blk][4 * g + 1] * myscale,
+                                oacc[blk][4 * g + 2] * myscale, oacc[blk][4 * g + 3] * myscale);
+            }
     }
-    for (int x = threadIdx.x; x < H * D; x += NT) {
-        const int h = x / D, dv = x % D;
-        float Mh = kNegInf, Lh = 0.f;
+    __syncthreads();
+    const bool o_vec = ((uintptr_t)a.o & 15) == 0;
+    for (int f = threadIdx.x; f < H * QN; f += NT) {
+        const int h = f / QN, q = f % QN;
+        const int slot = h * QN + (q ^ (h & (QN - 1)));
+        float4 sum = ((const float4*)&wl_s[0])[slot];
 #pragma unroll
-        for (int ww = 0; ww < NW; ++ww) Mh = fmaxf(Mh, ml_s[ww][h][0]);
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            const float mw = ml_s[ww][h][0];
-            Lh += mw == kNegInf ? 0.f : ml_s[ww][h][1] * exp2f(mw - Mh);
+        for (int ww = 1; ww < NW; ++ww) {
+            const float4 v = ((const float4*)&wl_s[ww])[slot];
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
         }
-        const float ov = obuf[h * D + dv];
         if (a.part) {
-            float* pp = a.part + (((int64_t)r * a.nsplit + split) * H + h) * (D + 2);
-            pp[dv] = ov;
-            if (dv == 0) { pp[D] = Mh; pp[D + 1] = Lh; }
+            *(float4*)(a.part + (((int64_t)r * a.nsplit + split) * H + h) * D + 4 * q) = sum;
         } else {
-            a.o[((int64_t)r * H + h) * D + dv] = Lh > 0.f ? ov / Lh : 0.f;
-            if (dv == 0 && a.lse) a.lse[(int64_t)r * H + h] = Lh > 0.f ? Mh + log2f(Lh) : kNegInf;
+            const float Lh = mlf_s[h][1];
+            const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
+            float* op = a.o + ((int64_t)r * H + h) * D + 4 * q;
+            if (o_vec) {
+                *(float4*)op = make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+            } else {
+                op[0] = sum.x * inv; op[1] = sum.y * inv; op[2] = sum.z * inv; op[3] = sum.w * inv;
+            }
         }
+    }
+    if (threadIdx.x < H) {
+        const float Mh = mlf_s[threadIdx.x][0], Lh = mlf_s[threadIdx.x][1];
+        if (a.part)
+            *(float2*)(a.part_ml + (((int64_t)r * a.nsplit + split) * H + threadIdx.x) * 2) = make_float2(Mh, Lh);
+        else if (a.lse)
+            a.lse[(int64_t)r * H + threadIdx.x] = Lh > 0.f ? Mh + log2f(Lh) : kNegInf;
     }
 }
 
@@ -289,10 +311,12 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(AttnArgs a) {
     __shared__ float wred[4];
     const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const float* base = a.part + ((int64_t)r * ns * H + h) * (D + 2);
-    const int64_t sstride = (int64_t)H * (D + 2);
+    // split s: o at obase + s * ostride, (m, l) at mbase + s * mstride
+    const float* obase = a.part + ((int64_t)r * ns * H + h) * D;
+    const float* mbase = a.part_ml + ((int64_t)r * ns * H + h) * 2;
+    const int64_t ostride = (int64_t)H * D, mstride = (int64_t)H * 2;
     float m = kNegInf;
-    for (int s = tid; s < ns; s += 256) m = fmaxf(m, base[s * sstride + D]);
+    for (int s = tid; s < ns; s += 256) m = fmaxf(m, mbase[s * mstride]);
     m = wave_max(m);
     if (lane == 0) wred[wv] = m;
     __syncthreads();
@@ -301,8 +325,8 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(AttnArgs a) {
     float l = 0.f;
     if (M != kNegInf)
         for (int s = tid; s < ns; s += 256) {
-            const float ms = base[s * sstride + D];
-            l += ms == kNegInf ? 0.f : base[s * sstride + D + 1] * exp2f(ms - M);
+            const float ms = mbase[s * mstride];
+            l += ms == kNegInf ? 0.f : mbase[s * mstride + 1] * exp2f(ms - M);
         }
     l = wave_sum(l);
     if (lane == 0) wred[wv] = l;
@@ -314,19 +338,16 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(AttnArgs a) {
     if (M != kNegInf) {
         int s = sl;
         for (; s + 48 < ns; s += 64) {
-            const float* p0 = base + s * sstride;
-            const float* p1 = p0 + 16 * sstride;
-            const float* p2 = p1 + 16 * sstride;
-            const float* p3 = p2 + 16 * sstride;
-            const float m0 = p0[D], m1 = p1[D], m2 = p2[D], m3 = p3[D];
-            const float o0 = p0[dv], o1 = p1[dv], o2 = p2[dv], o3 = p3[dv];
+            const float m0 = mbase[s * mstride], m1 = mbase[(s + 16) * mstride];
+            const float m2 = mbase[(s + 32) * mstride], m3 = mbase[(s + 48) * mstride];
+            const float o0 = obase[s * ostride + dv], o1 = obase[(s + 16) * ostride + dv];
+            const float o2 = obase[(s + 32) * ostride + dv], o3 = obase[(s + 48) * ostride + dv];
             acc += (m0 == kNegInf ? 0.f : o0 * exp2f(m0 - M)) + (m1 == kNegInf ? 0.f : o1 * exp2f(m1 - M)) +
                    (m2 == kNegInf ? 0.f : o2 * exp2f(m2 - M)) + (m3 == kNegInf ? 0.f : o3 * exp2f(m3 - M));
         }
         for (; s < ns; s += 16) {
-            const float* p = base + s * sstride;
-            const float ms = p[D];
-            if (ms != kNegInf) acc += p[dv] * exp2f(ms - M);
+            const float ms = mbase[s * mstride];
+            if (ms != kNegInf) acc += obase[s * ostride + dv] * exp2f(ms - M);
         }
     }
     red[sl][dl] = acc;
@@ -344,13 +365,21 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(AttnArgs a) {
 // ---- score pass --------------------------------------------------------------------------------
 // score(j) = sum_h 2^(x_h(j) - lse_h) for candidates j in [0, t - window]; S[head][key] = Q . K^T
 // so that every lane owns one key and sums its 16 heads, plus the partner lane's 16.
+//
+// K needs no LDS here: the B operand of lane (key n, half hb) at k-step s is 8 consecutive d
+// of key n, so each lane loads its operands straight from the cache row with 16-byte loads.
+// The d order inside the product is free as long as Q uses the same one; it is chosen so that
+// one load instruction covers 32 consecutive bytes of each of its 32 rows (one cache line per
+// row):  bf16: k-step s <-> d in [16s + 8hb, +8);  FP8: lane half hb holds d in [hb*D/2, +D/2),
+// k-step s <-> d in [hb*D/2 + 8s, +8).  NBUF tiles stay in flight per wave.
 template <int D, int KV>
-__global__ __launch_bounds__(256) void score_rows_mfma_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;
-    constexpr int NI = RawGeom<D, KV>::NI;
+    constexpr int ESZ = KV == HS2_FP8_E4M3 ? 1 : 2;
+    constexpr int RB = D * ESZ;                  // bytes per cache row
+    constexpr int NL = RB / 32;                  // 16-byte loads per lane per tile (half a row)
     constexpr int NBUF = KV == HS2_FP8_E4M3 ? 6 : 4;
     __shared__ uint32_t hist[kHistBins];
-    __shared__ __attribute__((aligned(16))) char tiles[kRowWaves][LdsTile<D>::BYTES];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 31, hb = lane >> 5;
     // splits run last-to-first: the attention pass streamed the cache first-to-last, so the
@@ -367,33 +396,63 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(ScoreArgs a) {
     if (a.rowhist)
         for (int x = threadIdx.x; x < kHistBins; x += 256) hist[x] = 0;
 
+    // Q rows and the normalisers are loaded unconditionally (clamped head, zeroed by select), so
+    // all of them are in flight together instead of one exec-masked load at a time
     bf16x8_t qop[KS];
     {
-        const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)a.q + ((int64_t)r * H + (n < H ? n : 0)) * D + hb * (D / 2));
+        const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)r * H + (n < H ? n : H - 1)) * D;
+        const uint32_t keep = n < H ? 0xffffffffu : 0u;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qop[s] = n < H ? __builtin_bit_cast(bf16x8_t, qp[s]) : bf16x8_t{};
+        for (int s = 0; s < KS; ++s) {
+            const int d0 = KV == HS2_FP8_E4M3 ? hb * (D / 2) + 8 * s : 16 * s + 8 * hb;
+            u32x4_t v = *(const u32x4_t*)(qrow + d0);
+            v[0] &= keep; v[1] &= keep; v[2] &= keep; v[3] &= keep;
+            qop[s] = __builtin_bit_cast(bf16x8_t, v);
+        }
     }
     // negative base-2 log normaliser of the 16 heads this lane sums: heads 8(i/4) + 4hb + i%4
     float nlse[16];
+    {
+        const float* lr = a.lse + (int64_t)r * H;
+        float raw[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int h = 8 * (i >> 2) + 4 * hb + (i & 3);
-        nlse[i] = h < H ? -a.lse[(int64_t)r * H + h] : kNegInf;
+        for (int i = 0; i < 16; ++i) {
+            const int h = 8 * (i >> 2) + 4 * hb + (i & 3);
+            raw[i] = lr[h < H ? h : H - 1];
+        }
+        // padded heads get -inf through arithmetic on the loaded value (a select would let the
+        // compiler turn the load back into a masked one)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nlse[i] = -raw[i] - (8 * (i >> 2) + 4 * hb + (i & 3) < H ? 0.f : kPosInf);
     }
     if (a.rowhist) __syncthreads();
 
-    char* klds = tiles[w];
-    u32x4_t kb[NBUF][NI];
+    u32x4_t kb[NBUF][NL];
     float ksb[NBUF];
     const int64_t ntw = ntiles > w ? (ntiles - w + kRowWaves - 1) / kRowWaves : 0;
-    const int64_t rowbase = (int64_t)b * a.Nmax;
-    // unconditional loads (rows clamped into the range, prefetches past the end re-load the
+    // bf16: load x of lane (n, hb) is row bytes [32x + 16hb, +16); FP8: [hb*RB/2 + 16x, +16)
+    const char* kbase = (const char*)a.k + (int64_t)b * a.Nmax * RB + (KV == HS2_FP8_E4M3 ? hb * (RB / 2) : 16 * hb);
+    constexpr int LSTRIDE = KV == HS2_FP8_E4M3 ? 16 : 32;
+    const float* ksbase = KV == HS2_FP8_E4M3 ? a.k_scale + (int64_t)b * a.Nmax : nullptr;
+    // unconditional loads (keys clamped into the range, prefetches past the end re-load the
     // wave's last tile) keep the compiler's load counting exact
     auto load = [&](u32x4_t* kr, float& ks, int64_t it) {
         const int64_t tl = w + (int64_t)kRowWaves * (it < ntw ? it : ntw - 1);
-        const int64_t te = e0 + 32 * tl;
-        load_raw_tile<D, KV>(kr, a.k, [&](int R) { return rowbase + (te + R < e1 ? te + R : e1 - 1); });
-        if (KV == HS2_FP8_E4M3) ks = a.k_scale[rowbase + (te + n < e1 ? te + n : e1 - 1)];
+        const int64_t j = e0 + 32 * tl + n < e1 ? e0 + 32 * tl + n : e1 - 1;
+        const char* p = kbase + j * RB;
+#pragma unroll
+        for (int x = 0; x < NL; ++x) kr[x] = *(const u32x4_t*)(p + LSTRIDE * x);
+        if (KV == HS2_FP8_E4M3) ks = ksbase[j];
+    };
+    auto kop = [&](const u32x4_t* kr, int s) -> bf16x8_t {
+        if (KV == HS2_FP8_E4M3) {
+            const u32x4_t c = kr[s >> 1];
+            const u32x2_t lo = fp8x4_to_bf16x4(c[2 * (s & 1)]), hi = fp8x4_to_bf16x4(c[2 * (s & 1) + 1]);
+            u32x4_t o;
+            o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
+            return __builtin_bit_cast(bf16x8_t, o);
+        }
+        return __builtin_bit_cast(bf16x8_t, kr[s]);
     };
     float* srow = a.scores + (int64_t)r * a.cstride;
     if (ntw > 0) {
@@ -406,19 +465,15 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(ScoreArgs a) {
                 load(kb[(u + NBUF - 1) % NBUF], ksb[(u + NBUF - 1) % NBUF], it + NBUF - 1);
                 if (it < ntw) {
                     const int64_t tile = w + (int64_t)kRowWaves * it;
-                    store_lds_tile<D, KV, false>(kb[u], klds, [](int) { return true; });
-                    wave_lds_fence();
                     f32x16_t sacc = f32x16_t{};
 #pragma unroll
                     for (int s = 0; s < KS; ++s)
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            qop[s], lds_row_operand<D>(klds, n, hb * (D / 16) + s), sacc, 0, 0, 0);
-                    wave_lds_fence();
+                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], kop(kb[u], s), sacc, 0, 0, 0);
                     float sc = a.scale_log2;
                     if (KV == HS2_FP8_E4M3) sc *= ksb[u];
                     float acc = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += exp2f(sacc[i] * sc + nlse[i]);
+                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sc, nlse[i]));
                     acc += __shfl_xor(acc, 32);
                     const int64_t j = e0 + 32 * tile + n;
                     if (hb == 0 && j < e1) {
@@ -437,22 +492,16 @@ __global__ __launch_bounds__(256) void score_rows_mfma_kernel(ScoreArgs a) {
 }
 
 // ---- launchers -------------------------------------------------------------------------------------
-template <int NW>
-static void launch_rows_nw(const AttnArgs& a, dim3 grid, hipStream_t s) {
-    if (a.kv_dtype == HS2_FP8_E4M3) {
-        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_FP8_E4M3, NW><<<grid, NW * 64, 0, s>>>(a);
-        else attn_rows_mfma_kernel<64, HS2_FP8_E4M3, NW><<<grid, NW * 64, 0, s>>>(a);
-    } else {
-        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_BF16, NW><<<grid, NW * 64, 0, s>>>(a);
-        else attn_rows_mfma_kernel<64, HS2_BF16, NW><<<grid, NW * 64, 0, s>>>(a);
-    }
-}
-
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s) {
     ProfScope ps(name, s);
     dim3 grid(a.B * a.Tq, a.nsplit);
-    if (a.waves == 8) launch_rows_nw<8>(a, grid, s);
-    else launch_rows_nw<4>(a, grid, s);
+    if (a.kv_dtype == HS2_FP8_E4M3) {
+        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_FP8_E4M3><<<grid, kRowWaves * 64, 0, s>>>(a);
+        else attn_rows_mfma_kernel<64, HS2_FP8_E4M3><<<grid, kRowWaves * 64, 0, s>>>(a);
+    } else {
+        if (a.d == 128) attn_rows_mfma_kernel<128, HS2_BF16><<<grid, kRowWaves * 64, 0, s>>>(a);
+        else attn_rows_mfma_kernel<64, HS2_BF16><<<grid, kRowWaves * 64, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 

@@ -9,6 +9,7 @@
 namespace hs2 {
 
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPosInf = __builtin_huge_valf();
 
 // ---- number formats ------------------------------------------------------------------------
 

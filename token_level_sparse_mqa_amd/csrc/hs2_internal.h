@@ -29,10 +29,12 @@ struct AttnArgs {
     int B, Tq, H, d; int64_t Nmax;
     float scale_log2;                    // sm_scale * log2(e): logits are kept in base 2
     int nsplit; int64_t chunk;           // key entries per split
-    float* part;                         // [R, nsplit, H, d + 2]: o, m, l of each split
+    // partial results of the splits.  VALU kernels: part [R, nsplit, H, d + 2] (o, m, l).
+    // MFMA kernels: part [R, nsplit, H, d] (o) and part_ml [R, nsplit, H, 2] (m, l).
+    float* part;
+    float* part_ml;
     float* o;                            // [R, H, d]
     float* lse;                          // [R, H] base-2 log-sum-exp (nullptr: not needed)
-    int waves;                           // waves per workgroup of the row kernel (4 or 8)
     uint32_t* zero_hist;                 // [R, kHistBins] to clear (nullptr: none)
     uint32_t* zero_cnt;                  // [R, 4] to clear
 };

@@ -26,7 +26,9 @@ __device__ __forceinline__ uint32_t dig3(uint32_t key) { return key & 0x3ffu; }
 
 // Given a histogram over nbins digits (LDS) and a rank k (1 <= k <= total), find the digit
 // holding the k-th largest entry and the number of entries with a larger digit.
-// res[0] = digit, res[1] = count above.  All threads of the block call it.
+// res[0] = digit, res[1] = count above.  All threads of the block call it.  Should the
+// histogram hold fewer than k entries, digit 0 is reported (exactly one thread writes res in
+// every case, so res never keeps stale values; callers bound their writes as well).
 template <int NT>
 __device__ void find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t* res, uint32_t* tmp) {
     const int per = (nbins + NT - 1) / NT;
@@ -37,7 +39,8 @@ __device__ void find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t
     uint32_t run = block_excl_scan<NT>(local, tmp, &total);
     for (int x = x0; x < x0 + per && x < nbins; ++x) {
         const uint32_t c = hist[nbins - 1 - x];
-        if (run < k && run + c >= k) { res[0] = (uint32_t)(nbins - 1 - x); res[1] = run; }
+        const bool last = x == nbins - 1;
+        if ((run < k && run + c >= k) || (last && run + c < k)) { res[0] = (uint32_t)(nbins - 1 - x); res[1] = run; }
         run += c;
     }
     __syncthreads();
@@ -124,8 +127,12 @@ __global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
         const int64_t j = j0 + u * 256 + threadIdx.x;
         if (j >= j1) continue;
         const uint32_t dg = dig1(key[u]);
-        if (dg > b1) a.sure[(int64_t)r * a.k_global + ps++] = (int32_t)j;
-        else if (dg == b1) {
+        if (dg > b1) {
+            // fewer than k_global entries lie above the k-th's bucket; the bound only matters
+            // if the row histogram disagreed with the scores
+            if (ps < (uint32_t)a.k_global) a.sure[(int64_t)r * a.k_global + ps] = (int32_t)j;
+            ++ps;
+        } else if (dg == b1) {
             if (pc < (uint32_t)kSelCap) a.cand[(int64_t)r * kSelCap + pc] = make_uint2(key[u], (uint32_t)j);
             ++pc;
         }
@@ -244,7 +251,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         const uint32_t n_eq = hist[b3];
         const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
         // sure picks from the gather pass
-        const uint32_t n_sure = above1;
+        const uint32_t n_sure = above1 < (uint32_t)K ? above1 : (uint32_t)K;
         for (uint32_t x = threadIdx.x; x < n_sure; x += kFinThreads) out[x] = a.sure[(int64_t)r * K + x];
         if (threadIdx.x == 0) { lcount[0] = n_sure; lcount[1] = 0; }
         // classify the bucket: above T -> picked; equal to T -> tie list (reusing ckey storage)
@@ -262,21 +269,27 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         for (int u = 0; u < kSelCap / kFinThreads; ++u) {
             const uint32_t x = threadIdx.x + u * kFinThreads;
             if (x < n_cand) {
-                if (myk[u] > T) out[atomicAdd(&lcount[0], 1u)] = myi[u];
-                else if (myk[u] == T) ties[atomicAdd(&lcount[1], 1u)] = myi[u];
+                if (myk[u] > T) {
+                    const uint32_t o = atomicAdd(&lcount[0], 1u);
+                    if (o < (uint32_t)K) out[o] = myi[u];
+                } else if (myk[u] == T) {
+                    ties[atomicAdd(&lcount[1], 1u)] = myi[u];   // at most n_cand <= kSelCap
+                }
             }
         }
         __syncthreads();
         const uint32_t base = lcount[0];
         if (need_eq == n_eq) {
-            for (uint32_t x = threadIdx.x; x < n_eq; x += kFinThreads) out[base + x] = ties[x];
+            for (uint32_t x = threadIdx.x; x < n_eq; x += kFinThreads)
+                if (base + x < (uint32_t)K) out[base + x] = ties[x];
         } else {
             int np = 1;
             while (np < (int)n_eq) np <<= 1;
             for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= (int)n_eq) ties[x] = 0x7fffffff;
             __syncthreads();
             bitonic_sort_i32(ties, np);
-            for (uint32_t x = threadIdx.x; x < need_eq; x += kFinThreads) out[base + x] = ties[x];
+            for (uint32_t x = threadIdx.x; x < need_eq && x < n_eq; x += kFinThreads)
+                if (base + x < (uint32_t)K) out[base + x] = ties[x];
         }
         __syncthreads();
         int np = 1;
@@ -328,7 +341,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         const bool pick = j < C && (key > T || (eq && rank < need_eq));
         uint32_t tot_pick;
         const uint32_t pos = run_out + block_excl_scan<kFinThreads>(pick ? 1u : 0u, tmp, &tot_pick);
-        if (pick) irow[pos] = (int32_t)j;
+        if (pick && pos < (uint32_t)K) irow[pos] = (int32_t)j;
         run_eq += tot_eq;
         run_out += tot_pick;
     }
