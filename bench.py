@@ -140,8 +140,7 @@ def run_gpu(cfg, steps, warmup, profile=True):
     kvd = hs2.dtype_code(t["k"])
     ws = torch.empty((hs2.hs2_full_attn_select_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global,
                                                                cfg.window, kvd),), dtype=torch.uint8, device=dev)
-    sws = torch.empty((hs2.hs2_sparse_attn_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S),),
-                      dtype=torch.uint8, device=dev)
+    sws = hs2.sparse_attn_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, dev)
     o = torch.empty((cfg.B, cfg.Tq, cfg.H, cfg.d), dtype=torch.float32, device=dev)
     idx = torch.empty((cfg.B, cfg.Tq, cfg.S), dtype=torch.int32, device=dev)
     o_sp = [torch.empty_like(o) for _ in range(cfg.n_sparse)]

@@ -90,8 +90,7 @@ class GpuRun:
         cfg = self.cfg
         ws = None
         if workspace:
-            n = self.hs2.hs2_sparse_attn_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, idx.shape[-1])
-            ws = torch.empty((n,), dtype=torch.uint8, device=self.q.device)
+            ws = self.hs2.sparse_attn_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, idx.shape[-1], self.q.device)
         return self.hs2.hs2_sparse_attn(self.qs[layer], self.k, self.v, idx, kv_len=self.kv_len,
                                         k_scale=self.k_scale, v_scale=self.v_scale, sm_scale=self.sm,
                                         workspace=ws)

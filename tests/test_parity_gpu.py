@@ -118,6 +118,27 @@ def test_deterministic_indices():
     assert torch.equal(idx1, idx2)
 
 
+def test_sparse_workspace_reuse():
+    """One sparse workspace reused by consecutive calls of different sizes gives the same bytes
+    as a fresh workspace per call."""
+    import token_level_sparse_mqa_amd as hs2
+    big = small_config("ws_reuse_big", 230, B=4, N=3000, Tq=2, n_sparse=1)
+    small = small_config("ws_reuse_small", 231, B=1, N=2000, Tq=1, n_sparse=1)
+    runs = []
+    for cfg in (big, small):
+        g = GpuRun(make_workload(cfg))
+        _, idx, _ = g.full()
+        runs.append((cfg, g, idx))
+    cfg0, g0, _ = runs[0]
+    shared = hs2.sparse_attn_workspace(cfg0.B, cfg0.Tq, cfg0.H, cfg0.d, cfg0.S, "cuda")
+    for rep in range(2):
+        for cfg, g, idx in runs:
+            ref = g.sparse(0, idx, workspace=True)
+            got = hs2.hs2_sparse_attn(g.qs[0], g.k, g.v, idx, kv_len=g.kv_len, sm_scale=g.sm, workspace=shared)
+            torch.cuda.synchronize()
+            assert torch.equal(ref, got), f"{cfg.name} pass {rep}: reused workspace changed the result"
+
+
 def test_empty_batch_is_noop():
     import token_level_sparse_mqa_amd as hs2
     q = torch.empty((0, 1, 32, 128), dtype=torch.bfloat16, device="cuda")

@@ -131,6 +131,12 @@ def hs2_sparse_attn_workspace_size(B: int, Tq: int, H: int, d: int, S: int) -> i
     return int(lib().hs2_sparse_attn_workspace_size(B, Tq, H, d, S))
 
 
+def sparse_attn_workspace(B: int, Tq: int, H: int, d: int, S: int, device) -> torch.Tensor:
+    """A workspace for hs2_sparse_attn (reusable across calls ordered on one stream)."""
+    n = hs2_sparse_attn_workspace_size(B, Tq, H, d, S)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device)
+
+
 def hs2_full_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
                          kv_len: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
                          v_scale: Optional[torch.Tensor] = None, k_global: int = 1024, window: int = 128,

@@ -25,6 +25,7 @@ namespace hs2 {
 
 constexpr int kRowWaves = 4;
 constexpr int kRowListMax = 1280;   // list entries per workgroup (list mode)
+constexpr int kCombineNarrowMax = 32;  // splits up to which a (row, head) workgroup merges alone
 
 // Registers of one tile in flight.
 template <int D, int KV>
@@ -302,11 +303,12 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     }
 }
 
-// ---- merge of the splits of each row --------------------------------------------------------------
-// Grid (row, head, D/16): 256 threads = 16 dims x 16 split lanes.  Every workgroup first reduces
-// the per-split maxima and sums of its head (tiny), then sums its 16 dims over the splits.
+// ---- merge of the splits of each row ----------------------------------------------------------------
+// Many splits (long rows): grid (row, head, D/16), 256 threads = 16 dims x 16 split lanes.  Every
+// workgroup first reduces the per-split maxima and sums of its head (tiny), then sums its 16
+// dims over the splits.
 template <int D>
-__global__ __launch_bounds__(256) void attn_split_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attn_split_combine_wide_kernel(AttnArgs a) {
     __shared__ float red[16][17];
     __shared__ float wred[4];
     const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
@@ -360,6 +362,48 @@ __global__ __launch_bounds__(256) void attn_split_combine_kernel(AttnArgs a) {
         a.o[((int64_t)r * H + h) * D + dvo] = Ltot > 0.f ? tot / Ltot : 0.f;
         if (dvo == 0 && a.lse) a.lse[(int64_t)r * H + h] = Ltot > 0.f ? M + log2f(Ltot) : kNegInf;
     }
+}
+
+// Few splits: one workgroup per (row, head), one thread per dv.  Splits are merged in batches of 16 whose
+// loads are all in flight together, with the running maximum rescaled between batches; the
+// (m, l) loads of a batch are the same for every thread of the workgroup.
+template <int D>
+__global__ __launch_bounds__(D) void attn_split_combine_kernel(AttnArgs a) {
+    constexpr int BATCH = 16;
+    const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
+    const int dv = threadIdx.x;
+    const float* obase = a.part + ((int64_t)r * ns * H + h) * D + dv;     // split s at + s * H * D
+    const float* mbase = a.part_ml + ((int64_t)r * ns * H + h) * 2;      // split s at + s * H * 2
+    float M = kNegInf, L = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < ns; s0 += BATCH) {
+        float2 ml[BATCH];
+        float ov[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const int sp = s0 + u < ns ? s0 + u : ns - 1;
+            ml[u] = *(const float2*)(mbase + (int64_t)sp * H * 2);
+            ov[u] = obase[(int64_t)sp * H * D];
+        }
+        float mb = kNegInf;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) if (s0 + u < ns) mb = fmaxf(mb, ml[u].x);
+        const float Mn = fmaxf(M, mb);
+        if (Mn == kNegInf) continue;                 // nothing seen yet
+        const float c = M == kNegInf ? 0.f : exp2f(M - Mn);
+        L *= c;
+        acc *= c;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            if (s0 + u < ns && ml[u].x != kNegInf) {
+                const float wgt = exp2f(ml[u].x - Mn);
+                L += ml[u].y * wgt;
+                acc += ov[u] * wgt;
+            }
+        }
+        M = Mn;
+    }
+    a.o[((int64_t)r * H + h) * D + dv] = L > 0.f ? acc / L : 0.f;
+    if (dv == 0 && a.lse) a.lse[(int64_t)r * H + h] = L > 0.f ? M + log2f(L) : kNegInf;
 }
 
 // ---- score pass --------------------------------------------------------------------------------
@@ -507,9 +551,15 @@ hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_
 
 hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s) {
     ProfScope ps(name, s);
-    dim3 grid(a.B * a.Tq, a.H, a.d / 16);
-    if (a.d == 128) attn_split_combine_kernel<128><<<grid, 256, 0, s>>>(a);
-    else attn_split_combine_kernel<64><<<grid, 256, 0, s>>>(a);
+    if (a.nsplit > kCombineNarrowMax) {
+        dim3 grid(a.B * a.Tq, a.H, a.d / 16);
+        if (a.d == 128) attn_split_combine_wide_kernel<128><<<grid, 256, 0, s>>>(a);
+        else attn_split_combine_wide_kernel<64><<<grid, 256, 0, s>>>(a);
+    } else {
+        dim3 grid(a.B * a.Tq, a.H);
+        if (a.d == 128) attn_split_combine_kernel<128><<<grid, 128, 0, s>>>(a);
+        else attn_split_combine_kernel<64><<<grid, 64, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
