@@ -24,13 +24,58 @@ __device__ __forceinline__ uint32_t dig1(uint32_t key) { return key >> 21; }
 __device__ __forceinline__ uint32_t dig2(uint32_t key) { return (key >> 10) & 0x7ffu; }
 __device__ __forceinline__ uint32_t dig3(uint32_t key) { return key & 0x3ffu; }
 
-// Given a histogram over nbins digits (LDS) and a rank k (1 <= k <= total), find the digit
-// holding the k-th largest entry and the number of entries with a larger digit.
-// res[0] = digit, res[1] = count above.  All threads of the block call it.  Should the
-// histogram hold fewer than k entries, digit 0 is reported (exactly one thread writes res in
-// every case, so res never keeps stale values; callers bound their writes as well).
+// Given a histogram over NBINS digits (global or LDS memory) and a rank k, find the digit
+// holding the k-th largest entry and the number of entries with a larger digit.  Every wave
+// that calls it computes the same result on its own (no barrier): lane l sums the NBINS/64
+// digits NBINS-1-l*PER .. NBINS-(l+1)*PER, a shuffle scan over the lanes gives each lane the
+// count above its digits, and the lane that holds the k-th entry broadcasts it.  Should the
+// histogram hold fewer than k entries, digit 0 is reported (callers bound their writes).
+template <int NBINS>
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k, uint32_t& digit, uint32_t& above) {
+    constexpr int PER = NBINS / 64;
+    const int lane = threadIdx.x & 63;
+    const uint32_t* hb = hist + NBINS - (lane + 1) * PER;   // this lane's digits, ascending
+    uint32_t c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i += 4) {
+        const uint4 q = *(const uint4*)(hb + i);
+        c[i] = q.x; c[i + 1] = q.y; c[i + 2] = q.z; c[i + 3] = q.w;
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) local += c[i];
+    uint32_t incl = local;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+    }
+    const uint32_t total = __shfl(incl, 63);
+    uint32_t run = incl - local;        // entries with a digit above this lane's digits
+    int found = -1;
+    uint32_t fab = 0;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {   // this lane's digits, descending
+        if (run < k && run + c[i] >= k) { found = NBINS - (lane + 1) * PER + i; fab = run; }
+        run += c[i];
+    }
+    const uint64_t m = __ballot(found >= 0);
+    if (m) {
+        const int src = __ffsll((unsigned long long)m) - 1;
+        digit = (uint32_t)__shfl(found, src);
+        above = __shfl(fab, src);
+    } else {
+        digit = 0;
+        above = total - __shfl(c[0], 63);    // lane 63 holds digits PER-1 .. 0
+    }
+}
+
+// Block-level digit search for a histogram in LDS: thread t reads consecutive digits (no bank
+// conflicts) and a block scan orders the threads.  Same result convention as wave_find_digit;
+// every thread of the block calls it and receives the result.
 template <int NT>
-__device__ void find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t* res, uint32_t* tmp) {
+__device__ void block_find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t& digit, uint32_t& above,
+                                 uint32_t* tmp, uint32_t* res) {
     const int per = (nbins + NT - 1) / NT;
     const int x0 = threadIdx.x * per;
     uint32_t local = 0;
@@ -44,6 +89,8 @@ __device__ void find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t
         run += c;
     }
     __syncthreads();
+    digit = res[0];
+    above = res[1];
 }
 
 __device__ __forceinline__ void row_info(const SelectArgs& a, int r, int64_t* t, int64_t* C) {
@@ -85,9 +132,7 @@ __global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
 // atomic per counter, then writes them (per-row counters stay uncontended).
 __global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
     constexpr int PER = kSelSeg / 256;
-    __shared__ uint32_t hist[kHistBins];
     __shared__ uint32_t tmp[8];
-    __shared__ uint32_t res[2];
     __shared__ uint32_t basev[2];
     const int r = blockIdx.x, seg = blockIdx.y;
     int64_t t, C;
@@ -96,10 +141,8 @@ __global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
     const int64_t j0 = (int64_t)seg * kSelSeg;
     if (j0 >= C) return;
     const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
-    for (int x = threadIdx.x; x < kHistBins; x += 256) hist[x] = a.rowhist[(int64_t)r * kHistBins + x];
-    __syncthreads();
-    find_digit<256>(hist, kHistBins, (uint32_t)a.k_global, res, tmp);
-    const uint32_t b1 = res[0];
+    uint32_t b1, above1;
+    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)a.k_global, b1, above1);
     const float* sc = a.scores + (int64_t)r * a.cstride;
     uint32_t key[PER];
     uint32_t ns = 0, nc = 0;
@@ -158,33 +201,48 @@ __device__ void bitonic_sort_i32(int32_t* v, int n) {
     }
 }
 
-// Ascending bitonic sort of n <= kFinThreads values, one per thread (thread i holds element i);
-// exchanges between lanes of a wave use shuffles, wider ones go through `buf` in LDS.
-// Returns this thread's element of the sorted sequence.
-__device__ int32_t bitonic_sort_1pt(int32_t v, int n, int32_t* buf) {
-    const int i = threadIdx.x;
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            int32_t other;
-            if (j >= 64) {
-                __syncthreads();
-                if (i < n) buf[i] = v;
-                __syncthreads();
-                other = (i < n) ? buf[i ^ j] : v;
-            } else {
-                other = __shfl_xor(v, j);
-            }
-            const bool up = (i & k) == 0;
-            const bool lower = (i & j) == 0;
-            if (i < n) v = (lower == up) ? min(v, other) : max(v, other);
-        }
-    }
+// Writes the K <= kFinThreads distinct picks out[0..K) (values in [0, C)) to irow in ascending
+// order.  Each pick goes to bucket v >> sh (at most kRankBuckets buckets cover [0, C)); a scan
+// of the bucket counts gives each bucket's first output position, and a pick's rank within its
+// bucket is the number of smaller picks there (buckets span 2^sh indices, so they hold few
+// picks unless the picks cluster).  cnt and start hold kRankBuckets entries, items K.
+constexpr int kRankBuckets = 4096;
+
+__device__ void rank_sort_picks(const int32_t* out, int K, int64_t C, int32_t* irow, uint32_t* cnt,
+                                uint32_t* start, int32_t* items, uint32_t* tmp) {
+    int sh = 0;
+    while (((C - 1) >> sh) >= kRankBuckets) ++sh;
+    for (int x = threadIdx.x; x < kRankBuckets; x += kFinThreads) cnt[x] = 0;
     __syncthreads();
-    return v;
+    const int t = threadIdx.x;
+    const int32_t v = t < K ? out[t] : -1;
+    const bool mine = v >= 0 && (int64_t)v < C;     // always, unless the counts disagreed
+    const int b = mine ? (int)((int64_t)v >> sh) : 0;
+    uint32_t slot = 0;
+    if (mine) slot = atomicAdd(&cnt[b], 1u);
+    __syncthreads();
+    constexpr int PER = kRankBuckets / kFinThreads;
+    uint32_t c[PER];
+    uint32_t sum = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) { c[i] = cnt[PER * t + i]; sum += c[i]; }
+    uint32_t total;
+    uint32_t base = block_excl_scan<kFinThreads>(sum, tmp, &total);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) { start[PER * t + i] = base; base += c[i]; }
+    __syncthreads();
+    if (mine) items[start[b] + slot] = v;
+    __syncthreads();
+    if (mine) {
+        const uint32_t s0 = start[b], n = cnt[b];
+        uint32_t rank = s0;
+        for (uint32_t i = 0; i < n; ++i) rank += items[s0 + i] < v ? 1u : 0u;
+        irow[rank] = v;
+    }
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a) {
-    __shared__ uint32_t hist[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint32_t ckey[kSelCap];
     __shared__ int32_t cidx[kSelCap];
     __shared__ int32_t out[4096];
@@ -220,10 +278,8 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         return;
     }
 
-    for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = a.rowhist[(int64_t)r * kHistBins + x];
-    __syncthreads();
-    find_digit<kFinThreads>(hist, kHistBins, (uint32_t)K, res, tmp);
-    const uint32_t b1 = res[0], above1 = res[1];
+    uint32_t b1, above1;
+    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)K, b1, above1);
     const uint32_t k1 = (uint32_t)K - above1;
     const uint32_t* cnt = a.counters + (int64_t)r * 4;
     const uint32_t n_cand = cnt[1];
@@ -237,16 +293,14 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         __syncthreads();
         for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads) atomicAdd(&hist[dig2(ckey[x])], 1u);
         __syncthreads();
-        find_digit<kFinThreads>(hist, kHistBins, k1, res, tmp);
-        b2 = res[0]; above2 = res[1];
+        block_find_digit<kFinThreads>(hist, kHistBins, k1, b2, above2, tmp, res);
         const uint32_t k2 = k1 - above2;
         for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
         __syncthreads();
         for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads)
             if (dig2(ckey[x]) == b2) atomicAdd(&hist[dig3(ckey[x])], 1u);
         __syncthreads();
-        find_digit<kFinThreads>(hist, 1024, k2, res, tmp);
-        b3 = res[0]; above3 = res[1];
+        block_find_digit<kFinThreads>(hist, 1024, k2, b3, above3, tmp, res);
         const uint32_t need_eq = k2 - above3;          // ties at T still needed
         const uint32_t n_eq = hist[b3];
         const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
@@ -292,14 +346,14 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
                 if (base + x < (uint32_t)K) out[base + x] = ties[x];
         }
         __syncthreads();
-        int np = 1;
-        while (np < K) np <<= 1;
-        for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= K) out[x] = 0x7fffffff;
-        __syncthreads();
-        if (np <= kFinThreads) {
-            const int32_t v = bitonic_sort_1pt(threadIdx.x < np ? out[threadIdx.x] : 0x7fffffff, np, out);
-            if (threadIdx.x < K) irow[threadIdx.x] = v;
+        if (K <= kFinThreads) {
+            // the candidate and histogram arrays are free now
+            rank_sort_picks(out, K, C, irow, ckey, (uint32_t*)cidx, (int32_t*)hist, tmp);
         } else {
+            int np = 1;
+            while (np < K) np <<= 1;
+            for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= K) out[x] = 0x7fffffff;
+            __syncthreads();
             bitonic_sort_i32(out, np);
             for (int x = threadIdx.x; x < K; x += kFinThreads) irow[x] = out[x];
         }
@@ -314,8 +368,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         if (dig1(key) == b1) atomicAdd(&hist[dig2(key)], 1u);
     }
     __syncthreads();
-    find_digit<kFinThreads>(hist, kHistBins, k1, res, tmp);
-    b2 = res[0]; above2 = res[1];
+    block_find_digit<kFinThreads>(hist, kHistBins, k1, b2, above2, tmp, res);
     const uint32_t k2 = k1 - above2;
     const uint32_t pre = (b1 << 11) | b2;
     for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
@@ -325,8 +378,7 @@ __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a
         if ((key >> 10) == pre) atomicAdd(&hist[dig3(key)], 1u);
     }
     __syncthreads();
-    find_digit<kFinThreads>(hist, 1024, k2, res, tmp);
-    b3 = res[0]; above3 = res[1];
+    block_find_digit<kFinThreads>(hist, 1024, k2, b3, above3, tmp, res);
     const uint32_t need_eq = k2 - above3;
     const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
     // ordered pass: ties ranked by index with a running block scan
