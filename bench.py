@@ -93,9 +93,9 @@ KERNEL_UNITS = {
     "bridge_mfma": ("bridge", "hbm"),
 }
 KERNEL_SOURCES = {
-    "full_attn_mfma": ["attn_mfma.hip", "mfma_tiles.h"],
+    "full_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "full_attn_prefill": ["attn_prefill.hip", "mfma_tiles.h"],
-    "sparse_attn_mfma": ["attn_mfma.hip", "mfma_tiles.h"],
+    "sparse_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "bridge_mfma": ["bridge_mfma.hip", "mfma_tiles.h"],
 }
 

@@ -25,7 +25,6 @@ namespace hs2 {
 
 constexpr int kRowWaves = 4;
 constexpr int kRowListMax = 1280;   // list entries per workgroup (list mode)
-constexpr int kCombineNarrowMax = 32;  // splits up to which a (row, head) workgroup merges alone
 
 // Registers of one tile in flight.
 template <int D, int KV>
@@ -303,239 +302,7 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     }
 }
 
-// ---- merge of the splits of each row ----------------------------------------------------------------
-// Many splits (long rows): grid (row, head, D/16), 256 threads = 16 dims x 16 split lanes.  Every
-// workgroup first reduces the per-split maxima and sums of its head (tiny), then sums its 16
-// dims over the splits.
-template <int D>
-__global__ __launch_bounds__(256) void attn_split_combine_wide_kernel(AttnArgs a) {
-    __shared__ float red[16][17];
-    __shared__ float wred[4];
-    const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // split s: o at obase + s * ostride, (m, l) at mbase + s * mstride
-    const float* obase = a.part + ((int64_t)r * ns * H + h) * D;
-    const float* mbase = a.part_ml + ((int64_t)r * ns * H + h) * 2;
-    const int64_t ostride = (int64_t)H * D, mstride = (int64_t)H * 2;
-    float m = kNegInf;
-    for (int s = tid; s < ns; s += 256) m = fmaxf(m, mbase[s * mstride]);
-    m = wave_max(m);
-    if (lane == 0) wred[wv] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-    __syncthreads();
-    float l = 0.f;
-    if (M != kNegInf)
-        for (int s = tid; s < ns; s += 256) {
-            const float ms = mbase[s * mstride];
-            l += ms == kNegInf ? 0.f : mbase[s * mstride + 1] * exp2f(ms - M);
-        }
-    l = wave_sum(l);
-    if (lane == 0) wred[wv] = l;
-    __syncthreads();
-    const float Ltot = wred[0] + wred[1] + wred[2] + wred[3];
-    const int dl = tid & 15, sl = tid >> 4;
-    const int dv = blockIdx.z * 16 + dl;
-    float acc = 0.f;
-    if (M != kNegInf) {
-        int s = sl;
-        for (; s + 48 < ns; s += 64) {
-            const float m0 = mbase[s * mstride], m1 = mbase[(s + 16) * mstride];
-            const float m2 = mbase[(s + 32) * mstride], m3 = mbase[(s + 48) * mstride];
-            const float o0 = obase[s * ostride + dv], o1 = obase[(s + 16) * ostride + dv];
-            const float o2 = obase[(s + 32) * ostride + dv], o3 = obase[(s + 48) * ostride + dv];
-            acc += (m0 == kNegInf ? 0.f : o0 * exp2f(m0 - M)) + (m1 == kNegInf ? 0.f : o1 * exp2f(m1 - M)) +
-                   (m2 == kNegInf ? 0.f : o2 * exp2f(m2 - M)) + (m3 == kNegInf ? 0.f : o3 * exp2f(m3 - M));
-        }
-        for (; s < ns; s += 16) {
-            const float ms = mbase[s * mstride];
-            if (ms != kNegInf) acc += obase[s * ostride + dv] * exp2f(ms - M);
-        }
-    }
-    red[sl][dl] = acc;
-    __syncthreads();
-    if (tid < 16) {
-        float tot = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) tot += red[q][tid];
-        const int dvo = blockIdx.z * 16 + tid;
-        a.o[((int64_t)r * H + h) * D + dvo] = Ltot > 0.f ? tot / Ltot : 0.f;
-        if (dvo == 0 && a.lse) a.lse[(int64_t)r * H + h] = Ltot > 0.f ? M + log2f(Ltot) : kNegInf;
-    }
-}
-
-// Few splits: one workgroup per (row, head), one thread per dv.  Splits are merged in batches of 16 whose
-// loads are all in flight together, with the running maximum rescaled between batches; the
-// (m, l) loads of a batch are the same for every thread of the workgroup.
-template <int D>
-__global__ __launch_bounds__(D) void attn_split_combine_kernel(AttnArgs a) {
-    constexpr int BATCH = 16;
-    const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
-    const int dv = threadIdx.x;
-    const float* obase = a.part + ((int64_t)r * ns * H + h) * D + dv;     // split s at + s * H * D
-    const float* mbase = a.part_ml + ((int64_t)r * ns * H + h) * 2;      // split s at + s * H * 2
-    float M = kNegInf, L = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += BATCH) {
-        float2 ml[BATCH];
-        float ov[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int sp = s0 + u < ns ? s0 + u : ns - 1;
-            ml[u] = *(const float2*)(mbase + (int64_t)sp * H * 2);
-            ov[u] = obase[(int64_t)sp * H * D];
-        }
-        float mb = kNegInf;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) if (s0 + u < ns) mb = fmaxf(mb, ml[u].x);
-        const float Mn = fmaxf(M, mb);
-        if (Mn == kNegInf) continue;                 // nothing seen yet
-        const float c = M == kNegInf ? 0.f : exp2f(M - Mn);
-        L *= c;
-        acc *= c;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            if (s0 + u < ns && ml[u].x != kNegInf) {
-                const float wgt = exp2f(ml[u].x - Mn);
-                L += ml[u].y * wgt;
-                acc += ov[u] * wgt;
-            }
-        }
-        M = Mn;
-    }
-    a.o[((int64_t)r * H + h) * D + dv] = L > 0.f ? acc / L : 0.f;
-    if (dv == 0 && a.lse) a.lse[(int64_t)r * H + h] = L > 0.f ? M + log2f(L) : kNegInf;
-}
-
-// ---- score pass --------------------------------------------------------------------------------
-// score(j) = sum_h 2^(x_h(j) - lse_h) for candidates j in [0, t - window]; S[head][key] = Q . K^T
-// so that every lane owns one key and sums its 16 heads, plus the partner lane's 16.
-//
-// K needs no LDS here: the B operand of lane (key n, half hb) at k-step s is 8 consecutive d
-// of key n, so each lane loads its operands straight from the cache row with 16-byte loads.
-// The d order inside the product is free as long as Q uses the same one; it is chosen so that
-// one load instruction covers 32 consecutive bytes of each of its 32 rows (one cache line per
-// row):  bf16: k-step s <-> d in [16s + 8hb, +8);  FP8: lane half hb holds d in [hb*D/2, +D/2),
-// k-step s <-> d in [hb*D/2 + 8s, +8).  NBUF tiles stay in flight per wave.
-template <int D, int KV>
-__global__ __launch_bounds__(256, 2) void score_rows_mfma_kernel(ScoreArgs a) {
-    constexpr int KS = D / 16;
-    constexpr int ESZ = KV == HS2_FP8_E4M3 ? 1 : 2;
-    constexpr int RB = D * ESZ;                  // bytes per cache row
-    constexpr int NL = RB / 32;                  // 16-byte loads per lane per tile (half a row)
-    constexpr int NBUF = KV == HS2_FP8_E4M3 ? 6 : 4;
-    __shared__ uint32_t hist[kHistBins];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const int n = lane & 31, hb = lane >> 5;
-    // splits run last-to-first: the attention pass streamed the cache first-to-last, so the
-    // keys it read last are the likeliest to still sit in the memory-side cache
-    const int r = blockIdx.x, split = gridDim.y - 1 - blockIdx.y;
-    const int b = r / a.Tq;
-    const int H = a.H;
-    const int64_t t = row_pos(a.q_pos, a.kv_len, r, a.Tq, a.Nmax);
-    const int64_t C = cand_count(t, a.window);
-    const int64_t e0 = (int64_t)split * a.chunk;
-    const int64_t e1 = e0 + a.chunk < C ? e0 + a.chunk : C;
-    if (e0 >= e1) return;
-    const int64_t ntiles = (e1 - e0 + 31) / 32;
-    if (a.rowhist)
-        for (int x = threadIdx.x; x < kHistBins; x += 256) hist[x] = 0;
-
-    // Q rows and the normalisers are loaded unconditionally (clamped head, zeroed by select), so
-    // all of them are in flight together instead of one exec-masked load at a time
-    bf16x8_t qop[KS];
-    {
-        const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)r * H + (n < H ? n : H - 1)) * D;
-        const uint32_t keep = n < H ? 0xffffffffu : 0u;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int d0 = KV == HS2_FP8_E4M3 ? hb * (D / 2) + 8 * s : 16 * s + 8 * hb;
-            u32x4_t v = *(const u32x4_t*)(qrow + d0);
-            v[0] &= keep; v[1] &= keep; v[2] &= keep; v[3] &= keep;
-            qop[s] = __builtin_bit_cast(bf16x8_t, v);
-        }
-    }
-    // negative base-2 log normaliser of the 16 heads this lane sums: heads 8(i/4) + 4hb + i%4
-    float nlse[16];
-    {
-        const float* lr = a.lse + (int64_t)r * H;
-        float raw[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int h = 8 * (i >> 2) + 4 * hb + (i & 3);
-            raw[i] = lr[h < H ? h : H - 1];
-        }
-        // padded heads get -inf through arithmetic on the loaded value (a select would let the
-        // compiler turn the load back into a masked one)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) nlse[i] = -raw[i] - (8 * (i >> 2) + 4 * hb + (i & 3) < H ? 0.f : kPosInf);
-    }
-    if (a.rowhist) __syncthreads();
-
-    u32x4_t kb[NBUF][NL];
-    float ksb[NBUF];
-    const int64_t ntw = ntiles > w ? (ntiles - w + kRowWaves - 1) / kRowWaves : 0;
-    // bf16: load x of lane (n, hb) is row bytes [32x + 16hb, +16); FP8: [hb*RB/2 + 16x, +16)
-    const char* kbase = (const char*)a.k + (int64_t)b * a.Nmax * RB + (KV == HS2_FP8_E4M3 ? hb * (RB / 2) : 16 * hb);
-    constexpr int LSTRIDE = KV == HS2_FP8_E4M3 ? 16 : 32;
-    const float* ksbase = KV == HS2_FP8_E4M3 ? a.k_scale + (int64_t)b * a.Nmax : nullptr;
-    // unconditional loads (keys clamped into the range, prefetches past the end re-load the
-    // wave's last tile) keep the compiler's load counting exact
-    auto load = [&](u32x4_t* kr, float& ks, int64_t it) {
-        const int64_t tl = w + (int64_t)kRowWaves * (it < ntw ? it : ntw - 1);
-        const int64_t j = e0 + 32 * tl + n < e1 ? e0 + 32 * tl + n : e1 - 1;
-        const char* p = kbase + j * RB;
-#pragma unroll
-        for (int x = 0; x < NL; ++x) kr[x] = *(const u32x4_t*)(p + LSTRIDE * x);
-        if (KV == HS2_FP8_E4M3) ks = ksbase[j];
-    };
-    auto kop = [&](const u32x4_t* kr, int s) -> bf16x8_t {
-        if (KV == HS2_FP8_E4M3) {
-            const u32x4_t c = kr[s >> 1];
-            const u32x2_t lo = fp8x4_to_bf16x4(c[2 * (s & 1)]), hi = fp8x4_to_bf16x4(c[2 * (s & 1) + 1]);
-            u32x4_t o;
-            o[0] = lo[0]; o[1] = lo[1]; o[2] = hi[0]; o[3] = hi[1];
-            return __builtin_bit_cast(bf16x8_t, o);
-        }
-        return __builtin_bit_cast(bf16x8_t, kr[s]);
-    };
-    float* srow = a.scores + (int64_t)r * a.cstride;
-    if (ntw > 0) {
-#pragma unroll
-        for (int u = 0; u < NBUF - 1; ++u) load(kb[u], ksb[u], u);
-        for (int64_t base = 0; base < ntw; base += NBUF) {
-#pragma unroll
-            for (int u = 0; u < NBUF; ++u) {
-                const int64_t it = base + u;
-                load(kb[(u + NBUF - 1) % NBUF], ksb[(u + NBUF - 1) % NBUF], it + NBUF - 1);
-                if (it < ntw) {
-                    const int64_t tile = w + (int64_t)kRowWaves * it;
-                    f32x16_t sacc = f32x16_t{};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], kop(kb[u], s), sacc, 0, 0, 0);
-                    float sc = a.scale_log2;
-                    if (KV == HS2_FP8_E4M3) sc *= ksb[u];
-                    float acc = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sc, nlse[i]));
-                    acc += __shfl_xor(acc, 32);
-                    const int64_t j = e0 + 32 * tile + n;
-                    if (hb == 0 && j < e1) {
-                        srow[j] = acc;
-                        if (a.rowhist) atomicAdd(&hist[__float_as_uint(acc) >> 21], 1u);
-                    }
-                }
-            }
-        }
-    }
-    if (a.rowhist) {
-        __syncthreads();
-        for (int x = threadIdx.x; x < kHistBins; x += 256)
-            if (hist[x]) atomicAdd(&a.rowhist[(int64_t)r * kHistBins + x], hist[x]);
-    }
-}
-
-// ---- launchers -------------------------------------------------------------------------------------
+// ---- launcher ------------------------------------------------------------------------------------
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s) {
     ProfScope ps(name, s);
     dim3 grid(a.B * a.Tq, a.nsplit);
@@ -545,33 +312,6 @@ hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_
     } else {
         if (a.d == 128) attn_rows_mfma_kernel<128, HS2_BF16><<<grid, kRowWaves * 64, 0, s>>>(a);
         else attn_rows_mfma_kernel<64, HS2_BF16><<<grid, kRowWaves * 64, 0, s>>>(a);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s) {
-    ProfScope ps(name, s);
-    if (a.nsplit > kCombineNarrowMax) {
-        dim3 grid(a.B * a.Tq, a.H, a.d / 16);
-        if (a.d == 128) attn_split_combine_wide_kernel<128><<<grid, 256, 0, s>>>(a);
-        else attn_split_combine_wide_kernel<64><<<grid, 256, 0, s>>>(a);
-    } else {
-        dim3 grid(a.B * a.Tq, a.H);
-        if (a.d == 128) attn_split_combine_kernel<128><<<grid, 128, 0, s>>>(a);
-        else attn_split_combine_kernel<64><<<grid, 64, 0, s>>>(a);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_score_rows_mfma(const ScoreArgs& a, hipStream_t s) {
-    ProfScope ps("score_rows_mfma", s);
-    dim3 grid(a.B * a.Tq, a.nsplit);
-    if (a.kv_dtype == HS2_FP8_E4M3) {
-        if (a.d == 128) score_rows_mfma_kernel<128, HS2_FP8_E4M3><<<grid, 256, 0, s>>>(a);
-        else score_rows_mfma_kernel<64, HS2_FP8_E4M3><<<grid, 256, 0, s>>>(a);
-    } else {
-        if (a.d == 128) score_rows_mfma_kernel<128, HS2_BF16><<<grid, 256, 0, s>>>(a);
-        else score_rows_mfma_kernel<64, HS2_BF16><<<grid, 256, 0, s>>>(a);
     }
     return hipGetLastError();
 }
