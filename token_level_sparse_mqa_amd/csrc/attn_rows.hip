@@ -86,6 +86,18 @@ __device__ __forceinline__ uint32_t stage_row_tile(const RowTile<D, KV>& T, RowW
     return valid;
 }
 
+// Lanes l and l ^ 32 hold the two halves of a head's keys: v_permlane32_swap gives every lane
+// both values without a trip through LDS.
+__device__ __forceinline__ float half_max(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// One 32-key tile: l_run is kept per lane half (the halves are added at the end).
 template <int D, int KV>
 __device__ __forceinline__ void row_tile_step(const RowWaveLds<D>& W, uint32_t valid, const char* qlds,
                                               f32x16_t* oacc, float& m_run, float& l_run, float sl2) {
@@ -120,7 +132,7 @@ __device__ __forceinline__ void row_tile_step(const RowWaveLds<D>& W, uint32_t v
         x[i] = ((valid >> m) & 1u) ? sacc[i] * sc : kNegInf;
         mt = fmaxf(mt, x[i]);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    mt = half_max(mt);
     const float mn = fmaxf(m_run, mt);
     const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
     // masked keys carry x = -inf and get weight exp2(-inf) = 0; while every key of a head has
@@ -132,7 +144,6 @@ __device__ __forceinline__ void row_tile_step(const RowWaveLds<D>& W, uint32_t v
         x[i] = __builtin_amdgcn_exp2f(x[i] - mref);
         ps += x[i];
     }
-    ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
     m_run = mn;
     if (KV == HS2_FP8_E4M3) {
@@ -236,6 +247,8 @@ void attn_rows_mfma_kernel(AttnArgs a) {
         row_tile_step<D, KV>(W, valid, q_s, oacc, m_run, l_run, sl2);
         wave_lds_fence();
     }
+
+    l_run = half_sum(l_run);
 
     // ---- merge the waves of the workgroup ----
     // every lane combines the (m, l) of its head n over the waves and keeps its own wave's scale
