@@ -147,14 +147,30 @@ __device__ __forceinline__ int64_t pf_rows(const int32_t* q_pos, const int32_t* 
 }
 
 // ---- pass 1 -------------------------------------------------------------------------------------
+// Lanes l and l ^ 32 hold the two halves of a head's keys: v_permlane32_swap gives every lane
+// both values without a trip through LDS.
+__device__ __forceinline__ float pf_half_max(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pf_half_sum(float x) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// One barrier per stage of SUB 32-key sub-tiles: each wave multiplies both sub-tiles, then runs
+// one online-softmax step over the 16 * SUB logits a lane holds for its head, so the barrier,
+// the maximum exchange and the rescale test are paid once per 64 keys.
 template <int D, int KV>
 __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a) {
     constexpr int KS = D / 16, NB = D / 32;
     constexpr int NX = PfGeom<D, KV>::NX;
-    constexpr int NST = 3;                       // tiles in flight in registers
-    __shared__ __attribute__((aligned(16))) char kt[2][LdsTile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) char vt[2][LdsTile<D>::BYTES];
-    __shared__ float ks_s[2][kTileRows], vs_s[2][kTileRows];
+    constexpr int SUB = 2;                       // 32-key sub-tiles per stage
+    constexpr int SK = SUB * kTileRows;          // keys per stage
+    constexpr int NST = 2;                       // stages in flight in registers
+    __shared__ __attribute__((aligned(16))) char kt[2][SUB][LdsTile<D>::BYTES];
+    __shared__ __attribute__((aligned(16))) char vt[2][SUB][LdsTile<D>::BYTES];
+    __shared__ float ks_s[2][SUB][kTileRows], vs_s[2][SUB][kTileRows];
     __shared__ int64_t t_s[kPfWaves];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -165,7 +181,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     const int64_t tmax = pf_rows(a.q_pos, a.kv_len, a.Tq, a.Nmax, b, i0, t_s);
     const int64_t t = t_s[w];
     const int r = b * a.Tq + (i0 + w < a.Tq ? i0 + w : a.Tq - 1);
-    const int64_t ntiles = (tmax + 1 + kTileRows - 1) / kTileRows;
+    const int64_t nstages = (tmax + 1 + SK - 1) / SK;
     const int64_t rowbase = (int64_t)b * a.Nmax;
     // the selection counters of these rows are cleared here (the score pass writes the whole
     // radix histogram of each row itself)
@@ -181,68 +197,84 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     f32x16_t oacc[NB];
 #pragma unroll
     for (int x = 0; x < NB; ++x) oacc[x] = f32x16_t{};
-    float m_run = kNegInf, l_run = 0.f;
+    float m_run = kNegInf, l_run = 0.f;          // l_run per lane half
     const float sl2 = a.scale_log2;
 
-    if (ntiles > 0) {
+    if (nstages > 0) {
         const int64_t khi = tmax + 1;
         const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
         const char* vseq = (const char*)a.v + rowbase * RawGeom<D, KV>::RB;
         const PfLoader<D, KV> ld;
-        u32x4_t rk[NST][NX], rv[NST][NX];
-        float rks[NST], rvs[NST];
-        auto load = [&](int st, int64_t tile) {
-            const int64_t tl = tile < ntiles ? tile : ntiles - 1;
-            ld.load(rk[st], kseq, tl * kTileRows, khi);
-            ld.load(rv[st], vseq, tl * kTileRows, khi);
-            if (KV == HS2_FP8_E4M3) {
-                const int64_t key = tl * kTileRows + (threadIdx.x & 31);
-                const int64_t kc = key < khi ? key : khi - 1;
-                rks[st] = a.k_scale[rowbase + kc];
-                rvs[st] = a.v_scale[rowbase + kc];
+        u32x4_t rk[NST][SUB][NX], rv[NST][SUB][NX];
+        float rks[NST][SUB], rvs[NST][SUB];
+        auto load = [&](int st, int64_t stage) {
+            const int64_t sg = stage < nstages ? stage : nstages - 1;
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                const int64_t k0 = sg * SK + sub * kTileRows;
+                ld.load(rk[st][sub], kseq, k0, khi);
+                ld.load(rv[st][sub], vseq, k0, khi);
+                if (KV == HS2_FP8_E4M3) {
+                    const int64_t key = k0 + (threadIdx.x & 31);
+                    const int64_t kc = key < khi ? key : khi - 1;
+                    rks[st][sub] = a.k_scale[rowbase + kc];
+                    rvs[st][sub] = a.v_scale[rowbase + kc];
+                }
             }
         };
         auto store = [&](int st, int buf) {
-            pf_store_k<D, KV>(rk[st], kt[buf]);
-            pf_store_v<D, KV>(rv[st], vt[buf]);
-            if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) { ks_s[buf][threadIdx.x] = rks[st]; vs_s[buf][threadIdx.x] = rvs[st]; }
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                pf_store_k<D, KV>(rk[st][sub], kt[buf][sub]);
+                pf_store_v<D, KV>(rv[st][sub], vt[buf][sub]);
+                if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) {
+                    ks_s[buf][sub][threadIdx.x] = rks[st][sub];
+                    vs_s[buf][sub][threadIdx.x] = rvs[st][sub];
+                }
+            }
         };
 #pragma unroll
         for (int u = 0; u < NST; ++u) load(u, u);
         store(0, 0);
         __syncthreads();
-        for (int64_t base = 0; base < ntiles; base += NST) {
+        for (int64_t base = 0; base < nstages; base += NST) {
 #pragma unroll
             for (int u = 0; u < NST; ++u) {
-                const int64_t tile = base + u;
-                if (tile >= ntiles) break;
-                const int buf = (int)(tile & 1);
-                const int64_t k0 = tile * kTileRows;
+                const int64_t stage = base + u;
+                if (stage >= nstages) break;
+                const int buf = (int)(stage & 1);
+                const int64_t k0 = stage * SK;
                 if (k0 <= t) {
-                    f32x16_t sacc = f32x16_t{};
+                    f32x16_t sacc[SUB];
 #pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_row_operand<D>(kt[buf], n, hb * (D / 16) + s),
-                                                                       qop[s], sacc, 0, 0, 0);
-                    // logits x = s * sc (sc > 0); keys past t are masked in the tile holding t
-                    float x[16];
-                    if (KV == HS2_FP8_E4M3) {
+                    for (int sub = 0; sub < SUB; ++sub) {
+                        sacc[sub] = f32x16_t{};
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) x[i] = sacc[i] * (sl2 * ks_s[buf][8 * (i >> 2) + 4 * hb + (i & 3)]);
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) x[i] = sacc[i];
+                        for (int s = 0; s < KS; ++s)
+                            sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                lds_row_operand<D>(kt[buf][sub], n, hb * (D / 16) + s), qop[s], sacc[sub], 0, 0, 0);
                     }
-                    if (k0 + kTileRows - 1 > t) {
+                    // logits x = s * sc (sc > 0); keys past t are masked in the stage holding t
+                    float x[16 * SUB];
+#pragma unroll
+                    for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            const int kr = 8 * (i >> 2) + 4 * hb + (i & 3);    // key row in the sub-tile
+                            x[16 * sub + i] = KV == HS2_FP8_E4M3 ? sacc[sub][i] * (sl2 * ks_s[buf][sub][kr]) : sacc[sub][i];
+                        }
+                    if (k0 + SK - 1 > t) {
                         const int lim = (int)(t - k0);
 #pragma unroll
-                        for (int i = 0; i < 16; ++i)
-                            if (8 * (i >> 2) + 4 * hb + (i & 3) > lim) x[i] = kNegInf;
+                        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                if (kTileRows * sub + 8 * (i >> 2) + 4 * hb + (i & 3) > lim) x[16 * sub + i] = kNegInf;
                     }
                     float mt = x[0];
 #pragma unroll
-                    for (int i = 1; i < 16; ++i) mt = fmaxf(mt, x[i]);
-                    mt = fmaxf(mt, __shfl_xor(mt, 32));
+                    for (int i = 1; i < 16 * SUB; ++i) mt = fmaxf(mt, x[i]);
+                    mt = pf_half_max(mt);
                     // bf16 path: x is still unscaled, scale the maximum (sc > 0 keeps the order)
                     const float scl = KV == HS2_FP8_E4M3 ? 1.f : sl2;
                     const float mn = fmaxf(m_run, mt * scl);
@@ -250,16 +282,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                     const float mref = (mn == kNegInf) ? 0.f : mn;
                     float ps = 0.f;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
+                    for (int i = 0; i < 16 * SUB; ++i) {
                         x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scl, -mref));
                         ps += x[i];
                     }
-                    ps += __shfl_xor(ps, 32);
                     l_run = l_run * alpha + ps;
                     m_run = mn;
                     if (KV == HS2_FP8_E4M3) {
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) x[i] *= vs_s[buf][8 * (i >> 2) + 4 * hb + (i & 3)];
+                        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) x[16 * sub + i] *= vs_s[buf][sub][8 * (i >> 2) + 4 * hb + (i & 3)];
                     }
                     if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -267,23 +300,31 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
 #pragma unroll
                             for (int i = 0; i < 16; ++i) oacc[blk][i] *= alpha;
                     }
-                    f16x8_t p[2];
+                    f16x8_t p[SUB][2];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) { p[0][e] = (_Float16)x[e]; p[1][e] = (_Float16)x[8 + e]; }
+                    for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            p[sub][0][e] = (_Float16)x[16 * sub + e];
+                            p[sub][1][e] = (_Float16)x[16 * sub + 8 + e];
+                        }
 #pragma unroll
                     for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-                        for (int ks = 0; ks < 2; ++ks)
-                            oacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lds_vt_operand_f16<D>(vt[buf], blk, ks),
-                                                                               p[ks], oacc[blk], 0, 0, 0);
+                        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                            for (int ks = 0; ks < 2; ++ks)
+                                oacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                    lds_vt_operand_f16<D>(vt[buf][sub], blk, ks), p[sub][ks], oacc[blk], 0, 0, 0);
                 }
-                // stage tile + 1 (registers (u+1) % NST) into the other buffer, refill stage u
-                if (tile + 1 < ntiles) store((u + 1) % NST, buf ^ 1);
-                load(u, tile + NST);
+                // stage + 1 (registers (u+1) % NST) into the other buffer, refill registers u
+                if (stage + 1 < nstages) store((u + 1) % NST, buf ^ 1);
+                load(u, stage + NST);
                 __syncthreads();
             }
         }
     }
+    l_run = pf_half_sum(l_run);
 
     // ---- finish: this workgroup saw every key of its rows ----
     if (i0 + w < a.Tq) {
