@@ -30,17 +30,14 @@ __device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w) {
     return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
 }
 
-// Upper halves of two fp32 -> packed bf16 pair (exact for bf16-representable values).
-__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
-    return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-}
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// Four E4M3 codes (one dword) -> four bf16 (two dwords).
+// Four E4M3 codes (one dword) -> four bf16 (two dwords), one conversion per pair.  bf16 holds
+// every E4M3 value exactly, so with scale 1 the result is the code's value.
 __device__ __forceinline__ u32x2_t fp8x4_to_bf16x4(uint32_t w) {
-    const f32x2_t a = fp8x2_to_f32<false>(w), b = fp8x2_to_f32<true>(w);
     u32x2_t r;
-    r[0] = pack_hi16(a[0], a[1]);
-    r[1] = pack_hi16(b[0], b[1]);
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
     return r;
 }
 
