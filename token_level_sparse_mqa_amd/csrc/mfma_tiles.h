@@ -58,8 +58,12 @@ __device__ __forceinline__ void wave_lds_fence() {
 
 // ---- the LDS tile: 32 rows of D 16-bit values ---------------------------------------------------
 // K tiles are read as 16-byte row chunks by 32 lanes at a time (chunk XOR row spreads them over
-// the banks); V tiles are read transposed, 4 consecutive rows x 2 adjacent chunks per 16-lane
-// group (chunk XOR 2 * (row mod 8) gives those 8 pieces 8 different bank groups).
+// the banks).  V tiles are read transposed: the two 16-lane groups of a half wave read the same
+// 4 consecutive rows, each group one pair of adjacent chunks per row, the second group's pair 2
+// chunks after the first's.  At D = 128 the chunk is XORed with 4 (row mod 4) + 2 ((row / 4) mod 2):
+// bit 1 of the XOR is the same for the 4 rows, so the 8 chunk pairs of the two groups land in 8
+// different bank groups.  At D = 64 (8 chunks a row) the XOR 2 (row mod 4) keeps each group free
+// of conflicts.  Any per-row XOR leaves the row-wise stores free of conflicts.
 template <int D>
 struct LdsTile {
     static constexpr int RB = D * 2;          // bytes per row
@@ -68,8 +72,11 @@ struct LdsTile {
     __device__ static __forceinline__ int off(int row, int chunk) {
         return row * RB + ((chunk ^ (row & (CPR - 1))) << 4);
     }
+    __device__ static __forceinline__ int vswz(int row) {
+        return CPR >= 16 ? (((row & 3) << 2) | (((row >> 2) & 1) << 1)) : ((row << 1) & (CPR - 2));
+    }
     __device__ static __forceinline__ int voff(int row, int chunk) {
-        return row * RB + ((chunk ^ ((row << 1) & (CPR - 2))) << 4);
+        return row * RB + ((chunk ^ vswz(row)) << 4);
     }
 };
 
