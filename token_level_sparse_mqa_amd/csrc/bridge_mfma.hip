@@ -18,40 +18,51 @@
 namespace hs2 {
 
 constexpr int kBrM = 256;          // token rows per workgroup
-constexpr int kBrK = 64;           // reduction chunk
 constexpr int kBrThreads = 512;    // eight waves
+constexpr int kBrK = 64;           // reduction chunk
+constexpr int kBrStages = 2;       // chunks in flight in registers (deeper pipelines measured slower)
 
-template <int DD>   // output columns per projection
+template <int DD, int BK>   // output columns per projection, reduction chunk
 struct BrGeom {
     static constexpr int N = 2 * DD;                 // K and V columns
     static constexpr int MB = 2;                     // MFMA row blocks per wave (64 rows)
     static constexpr int NB = DD / 32;               // MFMA column blocks per wave (d columns)
-    static constexpr int HROW = kBrK * 2;            // bytes per hidden-state row in LDS (8 chunks)
+    static constexpr int HROW = BK * 2;              // bytes per hidden-state row in LDS
+    static constexpr int HCPR = BK / 8;              // 16-byte chunks per hidden row
+    static constexpr int HRPB = 256 / HROW;          // hidden rows per 256-byte bank cycle
     static constexpr int WROW = N * 2;               // bytes per weight row in LDS
     static constexpr int WCPR = N / 8;               // 16-byte chunks per weight row
-    static constexpr int HBYTES = kBrM * HROW;       // 32 KB
-    static constexpr int WBYTES = kBrK * WROW;       // 32 KB (d = 128)
-    static constexpr int HCH = kBrM * (kBrK / 8);    // 16-byte chunks of a hidden chunk: 2048
-    static constexpr int WCH = kBrK * WCPR;          // 16-byte chunks of a weight chunk
-    static constexpr int HX = HCH / kBrThreads;      // 4
+    static constexpr int HBYTES = kBrM * HROW;
+    static constexpr int WBYTES = BK * WROW;
+    static constexpr int HCH = kBrM * HCPR;          // 16-byte chunks of a hidden chunk
+    static constexpr int WCH = BK * WCPR;            // 16-byte chunks of a weight chunk
+    static constexpr int HX = HCH / kBrThreads;
     static constexpr int WX = (WCH + kBrThreads - 1) / kBrThreads;
-    __device__ static __forceinline__ int hoff(int row, int chunk) { return row * HROW + ((chunk ^ (row & 7)) << 4); }
+    // An operand read covers 16 hidden rows (16 lanes, one chunk each), HRPB rows to a bank cycle:
+    // chunk XOR ((row / HRPB) mod HCPR) gives them 16 different bank groups.
+    __device__ static __forceinline__ int hoff(int row, int chunk) {
+        return row * HROW + ((chunk ^ ((row / HRPB) & (HCPR - 1))) << 4);
+    }
+    // Weight rows are read transposed: the two 16-lane groups of a half wave read the same 4 rows,
+    // the second group's chunk pair 2 chunks after the first's.  XOR 4 (row mod 4) + 2 ((row / 4)
+    // mod 2) keeps bit 1 equal over the 4 rows, so the 8 pairs land in 8 different bank groups.
     __device__ static __forceinline__ int woff(int row, int chunk) {
-        return row * WROW + ((chunk ^ ((row & 7) << 1)) << 4);
+        return row * WROW + ((chunk ^ (((row & 3) << 2) | (((row >> 2) & 1) << 1))) << 4);
     }
 };
 
-template <int DD>
+// BK-deep reduction chunks, NST of them in flight in registers: a chunk's loads are issued
+// NST - 1 chunks before it is stored to LDS, so NST - 1 chunk computations hide their latency.
+template <int DD, int BK, int NST>
 __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a) {
-    using G = BrGeom<DD>;
-    constexpr int NST = 2;
+    using G = BrGeom<DD, BK>;
     __shared__ __attribute__((aligned(16))) char hs[2][G::HBYTES];
     __shared__ __attribute__((aligned(16))) char ws[2][G::WBYTES];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = lane & 31, hb = lane >> 5;
     const int wm = w >> 1, wn = w & 1;                 // wave rows [64 wm, +64), columns [d wn, +d)
     const int64_t m0 = (int64_t)blockIdx.x * kBrM;
-    const int nk = a.D / kBrK;
+    const int nk = a.D / BK;
 
     // per-thread load slots: 32-bit byte offsets from the workgroup's first hidden row / weights
     const char* hbase = (const char*)(a.hidden + m0 * a.D);
@@ -60,7 +71,7 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
 #pragma unroll
     for (int x = 0; x < G::HX; ++x) {
         const int q = tid + x * kBrThreads;
-        const int row = q >> 3, c = q & 7;
+        const int row = q / G::HCPR, c = q % G::HCPR;
         const int64_t gr = m0 + row < a.T ? row : a.T - 1 - m0;
         hoffs[x] = (uint32_t)(gr * a.D * 2 + 16 * c);
         hst[x] = G::hoff(row, c);
@@ -81,8 +92,8 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
     u32x4_t rh[NST][G::HX], rw[NST][G::WX];
     auto load = [&](int st, int kc) {
         kc = kc < nk ? kc : nk - 1;
-        const uint32_t hk = (uint32_t)kc * kBrK * 2;               // bytes along a hidden row
-        const uint32_t wk = (uint32_t)kc * kBrK * DD * 2;          // bytes down the weights
+        const uint32_t hk = (uint32_t)kc * BK * 2;                 // bytes along a hidden row
+        const uint32_t wk = (uint32_t)kc * BK * DD * 2;            // bytes down the weights
 #pragma unroll
         for (int x = 0; x < G::HX; ++x) rh[st][x] = *(const u32x4_t*)(hbase + (hoffs[x] + hk));
 #pragma unroll
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
             const char* hb_ = hs[buf];
             const char* wb_ = ws[buf];
 #pragma unroll
-            for (int ks = 0; ks < kBrK / 16; ++ks) {
+            for (int ks = 0; ks < BK / 16; ++ks) {
                 // A: hidden rows 64 wm + 32 i + n, d = 16 ks + 8 hb + {0..7}
                 bf16x8_t aop[G::MB];
 #pragma unroll
@@ -167,8 +178,8 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s) {
     ProfScope ps("bridge_mfma", s);
     dim3 grid((unsigned)((a.T + kBrM - 1) / kBrM));
-    if (a.d == 128) bridge_mfma_kernel<128><<<grid, kBrThreads, 0, s>>>(a);
-    else bridge_mfma_kernel<64><<<grid, kBrThreads, 0, s>>>(a);
+    if (a.d == 128) bridge_mfma_kernel<128, kBrK, kBrStages><<<grid, kBrThreads, 0, s>>>(a);
+    else bridge_mfma_kernel<64, kBrK, kBrStages><<<grid, kBrThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
