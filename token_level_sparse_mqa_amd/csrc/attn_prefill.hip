@@ -5,14 +5,14 @@
 // workgroup share every K/V tile: the tile is read from memory once into LDS and all eight
 // waves (one query token each, its 32 heads as the MFMA N dimension) multiply against it.
 //
-// Pass 1 per wave and 32-key tile:
-//   S^T = K_tile . Q^T (bf16 MFMA), causal mask key <= t, online softmax in base 2,
-//   O^T += V^T . P^T with V staged in LDS as fp16 and P rounded to fp16 (fp16 MFMA).
-// Pass 2 (score) per wave and tile:
+// Pass 1 per wave and 64-key stage:
+//   S^T = K_stage . Q^T (bf16 MFMA), causal mask key <= t, online softmax in base 2,
+//   O^T += V^T . P^T with V^T built in LDS as fp16 and P rounded to fp16 (fp16 MFMA).
+// Pass 2 (score) per wave and 32-key tile:
 //   S = Q . K_tile^T, score(j) = sum_h 2^(x_h(j) - lse_h), a per-row radix histogram in LDS.
 //
-// Workgroup tiles are double-buffered in LDS; the cooperative global loads of the next tiles
-// are kept in flight in registers (unconditional, clamped loads) while a tile is computed.
+// The cooperative global loads of the next tiles are kept in flight in registers
+// (unconditional, clamped loads) while a tile is computed.
 #include "mfma_tiles.h"
 
 namespace hs2 {
@@ -22,30 +22,40 @@ typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 constexpr int kPfWaves = 8;                  // query tokens (waves) per workgroup
 constexpr int kPfThreads = kPfWaves * 64;
 
-// Geometry of the cooperative (workgroup-wide) loads of one tile in storage format.
-template <int D, int KV>
+// Geometry of the cooperative loads of one 32-row tile in storage format by NT threads.
+template <int D, int KV, int NT>
 struct PfGeom {
     using G = RawGeom<D, KV>;
     static constexpr int CHUNKS = kTileRows * G::CPR;                    // 16-byte chunks per tile
-    static constexpr int NX = (CHUNKS + kPfThreads - 1) / kPfThreads;    // loads per thread
+    static constexpr int NX = (CHUNKS + NT - 1) / NT;                    // loads per thread
 };
 
 // Per-thread part of the cooperative tile loads: load x of a thread reads 16-byte chunk c of tile
 // row R, at byte offset (k0 + R) * RB + 16 c from the sequence's first cache row.  Offsets are
 // 32-bit (the host keeps Nmax * row bytes below 2^31).
-template <int D, int KV>
+template <int D, int KV, int NT>
 struct PfLoader {
     using G = RawGeom<D, KV>;
-    using P = PfGeom<D, KV>;
+    using P = PfGeom<D, KV, NT>;
     uint32_t off[P::NX];      // R * RB + 16 c
     int R[P::NX];
-    __device__ __forceinline__ PfLoader() {
+    __device__ __forceinline__ explicit PfLoader(int tid) {
 #pragma unroll
         for (int x = 0; x < P::NX; ++x) {
-            int q = threadIdx.x + x * kPfThreads;
+            int q = tid + x * NT;
             q = q < P::CHUNKS ? q : P::CHUNKS - 1;
             R[x] = q / G::CPR;
             off[x] = (uint32_t)(R[x] * G::RB + 16 * (q % G::CPR));
+        }
+    }
+    // rows k0 .. k0+31, rows at or past khi read row khi - 1 instead; no branch, so the loads can
+    // be scheduled among other work
+    __device__ __forceinline__ void load_clamped(u32x4_t* raw, const char* seq, int64_t k0, int64_t khi) const {
+        const uint32_t lim = (uint32_t)(khi - 1), kb = (uint32_t)k0;
+#pragma unroll
+        for (int x = 0; x < P::NX; ++x) {
+            const uint32_t key = kb + R[x] < lim ? kb + R[x] : lim;
+            raw[x] = *(const u32x4_t*)(seq + (key * G::RB + (off[x] - (uint32_t)R[x] * G::RB)));
         }
     }
     // rows k0 .. k0+31; rows at or past khi read row khi - 1 instead
@@ -64,15 +74,22 @@ struct PfLoader {
     }
 };
 
+// Byte offset of 16-byte chunk `chunk` of LDS tile row `row`: the swizzled LdsTile layout
+// (ST = 0) or rows padded to a stride of ST bytes.
+template <int D, int ST>
+__device__ __forceinline__ int pf_koff(int row, int chunk) {
+    if (ST > 0) return row * ST + 16 * chunk;
+    return LdsTile<D>::off(row, chunk);
+}
+
 // bf16 LDS tile from raw K (FP8 codes converted exactly).
-template <int D, int KV>
-__device__ __forceinline__ void pf_store_k(const u32x4_t* raw, char* lds) {
+template <int D, int KV, int NT, int ST>
+__device__ __forceinline__ void pf_store_k(const u32x4_t* raw, char* lds, int tid) {
     using G = RawGeom<D, KV>;
-    using P = PfGeom<D, KV>;
-    using T = LdsTile<D>;
+    using P = PfGeom<D, KV, NT>;
 #pragma unroll
     for (int x = 0; x < P::NX; ++x) {
-        const int q = threadIdx.x + x * kPfThreads;
+        const int q = tid + x * NT;
         if (q >= P::CHUNKS) continue;
         const int R = q / G::CPR, c = q % G::CPR;
         if (KV == HS2_FP8_E4M3) {
@@ -81,10 +98,10 @@ __device__ __forceinline__ void pf_store_k(const u32x4_t* raw, char* lds) {
             const u32x2_t cc = fp8x4_to_bf16x4(raw[x][2]), d = fp8x4_to_bf16x4(raw[x][3]);
             lo[0] = a[0]; lo[1] = a[1]; lo[2] = b[0]; lo[3] = b[1];
             hi[0] = cc[0]; hi[1] = cc[1]; hi[2] = d[0]; hi[3] = d[1];
-            *(u32x4_t*)(lds + T::off(R, 2 * c)) = lo;
-            *(u32x4_t*)(lds + T::off(R, 2 * c + 1)) = hi;
+            *(u32x4_t*)(lds + pf_koff<D, ST>(R, 2 * c)) = lo;
+            *(u32x4_t*)(lds + pf_koff<D, ST>(R, 2 * c + 1)) = hi;
         } else {
-            *(u32x4_t*)(lds + T::off(R, c)) = raw[x];
+            *(u32x4_t*)(lds + pf_koff<D, ST>(R, c)) = raw[x];
         }
     }
 }
@@ -93,16 +110,16 @@ __device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-// fp16 LDS tile from raw V.  bf16 -> fp16 is exact for |v| in [2^-14, 65504]; smaller values
-// keep an absolute error below 2^-25, larger ones saturate.  FP8 codes convert exactly.
-template <int D, int KV>
-__device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds) {
+// fp16 LDS tile from raw V, rows at a stride of ST bytes.  bf16 -> fp16 is exact for |v| in
+// [2^-14, 65504]; smaller values keep an absolute error below 2^-25, larger ones saturate.  FP8
+// codes convert exactly.
+template <int D, int KV, int NT, int ST>
+__device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds, int tid) {
     using G = RawGeom<D, KV>;
-    using P = PfGeom<D, KV>;
-    using T = LdsTile<D>;
+    using P = PfGeom<D, KV, NT>;
 #pragma unroll
     for (int x = 0; x < P::NX; ++x) {
-        const int q = threadIdx.x + x * kPfThreads;
+        const int q = tid + x * NT;
         if (q >= P::CHUNKS) continue;
         const int R = q / G::CPR, c = q % G::CPR;
         if (KV == HS2_FP8_E4M3) {
@@ -113,8 +130,8 @@ __device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds) {
                 const uint32_t p0 = f16x2_bits(a[0], a[1]), p1 = f16x2_bits(b[0], b[1]);
                 if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; } else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
             }
-            *(u32x4_t*)(lds + T::voff(R, 2 * c)) = lo;
-            *(u32x4_t*)(lds + T::voff(R, 2 * c + 1)) = hi;
+            *(u32x4_t*)(lds + R * ST + 32 * c) = lo;
+            *(u32x4_t*)(lds + R * ST + 32 * c + 16) = hi;
         } else {
             u32x4_t o;
 #pragma unroll
@@ -122,15 +139,24 @@ __device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds) {
                 const uint32_t u = raw[x][w];
                 o[w] = f16x2_bits(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
             }
-            *(u32x4_t*)(lds + T::voff(R, c)) = o;
+            *(u32x4_t*)(lds + R * ST + 16 * c) = o;
         }
     }
 }
 
+// LDS tiles of the attention pass, rows padded instead of swizzled so that every operand read of
+// a stage is one base address plus an immediate offset.
+//   K:   key rows, stride 2D + 16 bytes (8 consecutive rows of a b128 read start 4 banks apart).
+//   V^T: one row per dim with the sub-tile's 32 keys, stride 80 bytes (the rows of 8 lanes of a
+//        b128 read cover disjoint banks).  Keys are stored in the order the P operand uses:
+//        within each 16-key step, positions 8 hb + j hold key 8 (j / 4) + 4 hb + j % 4, so a
+//        lane's 8 operand values are one 16-byte chunk.
+//   V staging: key rows, stride 2D + 64 bytes, read once with transposing reads to build V^T.
 template <int D>
-__device__ __forceinline__ f16x8_t lds_vt_operand_f16(const char* lds, int blk, int ks) {
-    return __builtin_bit_cast(f16x8_t, lds_vt_operand<D>(lds, blk, ks));
-}
+struct PfTiles {
+    static constexpr int KST = 2 * D + 16, VTST = 80, VST = 2 * D + 64;
+    static constexpr int KB = kTileRows * KST, VTB = D * VTST, VB = kTileRows * VST;
+};
 
 // Positions of the workgroup's query rows; returns the largest one (or -1).
 __device__ __forceinline__ int64_t pf_rows(const int32_t* q_pos, const int32_t* kv_len, int Tq, int64_t Nmax,
@@ -158,30 +184,63 @@ __device__ __forceinline__ float pf_half_sum(float x) {
     return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-// One barrier per stage of SUB 32-key sub-tiles: each wave multiplies both sub-tiles, then runs
-// one online-softmax step over the 16 * SUB logits a lane holds for its head, so the barrier,
-// the maximum exchange and the rescale test are paid once per 64 keys.
+// Two wave groups of four waves share each SIMD pairwise and run half a stage apart: while one
+// group multiplies (P.V of the previous stage, then S of the current one) the other runs the
+// online softmax of its last S, so the matrix cores and the vector ALUs work at the same time.
+// A workgroup barrier closes every half-stage.  Group g loads, stages and transposes sub-tile g
+// of every stage.
+//
+// Half-step h, group g, e = h - g:
+//   e = 2m:    O += P(m-1).V(m-1) and S(m) = K(m).Q as one software-pipelined MFMA sequence
+//              (LDS operands read a few MFMAs ahead); in its middle the group stores its K rows
+//              and staged V rows of stage m+1 and issues the loads of stage m+2.  The wave runs
+//              at raised priority so that its MFMAs are not starved by the other group's VALU.
+//   e = 2m+1:  transposing reads of the staged V rows of stage m+1, then P(m) = softmax step on
+//              S(m), then the V^T writes of stage m+1.
+// Three LDS stage buffers cover a stage's lifetime (K is read during the two halves of its own
+// stage, V^T during the next two).  V^T costs one transposing read per element per workgroup;
+// reading V transposed in every wave would cost eight, at half the rate of b128 reads.
+//
+// The softmax keeps a lazy reference point per head: the weights 2^(x - ref) of a stage are
+// computed against the stored reference and kept if every lane's 32 weights sum to at most
+// kPfWeightMax (so P <= 2^8, well inside fp16); only otherwise does it take the stage maximum,
+// move the reference and rescale O and l.  The per-stage maximum and rescale are skipped on
+// nearly every stage.
+constexpr float kPfWeightMax = 256.f;
+constexpr int kPfAhead = 4;                 // LDS operand reads in flight ahead of the MFMAs
+constexpr int kPfMid = 7;                    // MFMA item after which the next sub-tile is stored
+
+// Waves w and w + 4 of a workgroup run on the same SIMD: the groups are w / 4.
+__device__ __forceinline__ int pf_group(int w) { return w >> 2; }
+__device__ __forceinline__ int pf_gtid(int w, int lane) { return (w & 3) * 64 + lane; }
+
 template <int D, int KV>
 __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a) {
     constexpr int KS = D / 16, NB = D / 32;
-    constexpr int NX = PfGeom<D, KV>::NX;
-    constexpr int SUB = 2;                       // 32-key sub-tiles per stage
+    constexpr int NT = kPfThreads / 2;           // threads per wave group
+    constexpr int NX = PfGeom<D, KV, NT>::NX;
+    constexpr int SUB = 2;                       // 32-key sub-tiles per stage (one per group)
     constexpr int SK = SUB * kTileRows;          // keys per stage
-    constexpr int NST = 2;                       // stages in flight in registers
-    __shared__ __attribute__((aligned(16))) char kt[2][SUB][LdsTile<D>::BYTES];
-    __shared__ __attribute__((aligned(16))) char vt[2][SUB][LdsTile<D>::BYTES];
-    __shared__ float ks_s[2][SUB][kTileRows], vs_s[2][SUB][kTileRows];
+    constexpr int NBUF = 3;                      // LDS stage buffers
+    using TL = PfTiles<D>;
+    __shared__ __attribute__((aligned(16))) char kt[NBUF][SUB][TL::KB];
+    __shared__ __attribute__((aligned(16))) char vt[NBUF][SUB][TL::VTB];
+    __shared__ __attribute__((aligned(16))) char vstage[SUB][TL::VB];
+    __shared__ float ks_s[NBUF][SUB][kTileRows], vs_s[NBUF][SUB][kTileRows];
     __shared__ int64_t t_s[kPfWaves];
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 31, hb = lane >> 5;
+    const int grp = pf_group(w);
+    const int gtid = pf_gtid(w, lane);           // thread index inside the group
     const int nqt = (a.Tq + kPfWaves - 1) / kPfWaves;
     const int b = blockIdx.x / nqt, i0 = (blockIdx.x % nqt) * kPfWaves;
     const int H = a.H;
     const int64_t tmax = pf_rows(a.q_pos, a.kv_len, a.Tq, a.Nmax, b, i0, t_s);
     const int64_t t = t_s[w];
     const int r = b * a.Tq + (i0 + w < a.Tq ? i0 + w : a.Tq - 1);
-    const int64_t nstages = (tmax + 1 + SK - 1) / SK;
+    const int nstages = __builtin_amdgcn_readfirstlane((int)((tmax + 1 + SK - 1) / SK));
+    const int last = __builtin_amdgcn_readfirstlane(t >= 0 ? (int)(t / SK) : -1);   // last stage this wave computes
     const int64_t rowbase = (int64_t)b * a.Nmax;
     // the selection counters of these rows are cleared here (the score pass writes the whole
     // radix histogram of each row itself)
@@ -197,131 +256,261 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     f32x16_t oacc[NB];
 #pragma unroll
     for (int x = 0; x < NB; ++x) oacc[x] = f32x16_t{};
-    float m_run = kNegInf, l_run = 0.f;          // l_run per lane half
+    float m_ref = kNegInf, l_run = 0.f;          // l_run per lane half
     const float sl2 = a.scale_log2;
 
     if (nstages > 0) {
         const int64_t khi = tmax + 1;
         const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
         const char* vseq = (const char*)a.v + rowbase * RawGeom<D, KV>::RB;
-        const PfLoader<D, KV> ld;
-        u32x4_t rk[NST][SUB][NX], rv[NST][SUB][NX];
-        float rks[NST][SUB], rvs[NST][SUB];
-        auto load = [&](int st, int64_t stage) {
-            const int64_t sg = stage < nstages ? stage : nstages - 1;
+        const PfLoader<D, KV, NT> ld(gtid);
+        u32x4_t rk[NX], rv[NX];
+        float rks = 0.f, rvs = 0.f;
+        // this group's sub-tile of a stage, clamped into the key range
+        auto load = [&](int stage) {
+            const int sg = stage < nstages ? stage : nstages - 1;
+            const int64_t k0 = (int64_t)sg * SK + grp * kTileRows;
+            ld.load_clamped(rk, kseq, k0, khi);
+            ld.load_clamped(rv, vseq, k0, khi);
+            if (KV == HS2_FP8_E4M3) {
+                const int64_t key = k0 + (gtid & 31);
+                const int64_t kc = key < khi ? key : khi - 1;
+                rks = a.k_scale[rowbase + kc];
+                rvs = a.v_scale[rowbase + kc];
+            }
+        };
+        auto store = [&](int buf) {
+            pf_store_k<D, KV, NT, TL::KST>(rk, kt[buf][grp], gtid);
+            pf_store_v<D, KV, NT, TL::VST>(rv, vstage[grp], gtid);
+            if (KV == HS2_FP8_E4M3 && gtid < kTileRows) {
+                ks_s[buf][grp][gtid] = rks;
+                vs_s[buf][grp][gtid] = rvs;
+            }
+        };
+        // V^T of this group's sub-tile from the staged rows: wave w % 4 builds (dv block, key step)
+        // pairs c = w % 4 + 4 u; the two transposing reads give lane (G, q) dim 32 blk + lane % 32
+        // of keys 16 ks + 4 hb + {0..3} and 16 ks + 8 + 4 hb + {0..3}.  Split into reads and writes
+        // so that the softmax math runs while the reads are in flight.
+        constexpr int NTU = (NB * 2 + 3) / 4;    // pairs per wave
+        auto t_read = [&](u32x4_t* rr) {
+            const int G = lane >> 4, q = lane & 15;
+            const char* src = vstage[grp] + (4 * hb + (q >> 2)) * TL::VST + (16 * (G & 1) + 4 * (q & 3)) * 2;
 #pragma unroll
-            for (int sub = 0; sub < SUB; ++sub) {
-                const int64_t k0 = sg * SK + sub * kTileRows;
-                ld.load(rk[st][sub], kseq, k0, khi);
-                ld.load(rv[st][sub], vseq, k0, khi);
-                if (KV == HS2_FP8_E4M3) {
-                    const int64_t key = k0 + (threadIdx.x & 31);
-                    const int64_t kc = key < khi ? key : khi - 1;
-                    rks[st][sub] = a.k_scale[rowbase + kc];
-                    rvs[st][sub] = a.v_scale[rowbase + kc];
+            for (int u = 0; u < NTU; ++u) {
+                const int cc = 4 * u + (w & 3);
+                const int blk = (cc < NB * 2 ? cc : 0) >> 1, ks = cc & 1;
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const char* pp = src + (16 * ks + 8 * h2) * TL::VST + blk * 64;
+                    const u32x2_t tu = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)pp));
+                    rr[u][2 * h2] = tu[0];
+                    rr[u][2 * h2 + 1] = tu[1];
                 }
             }
         };
-        auto store = [&](int st, int buf) {
+        auto t_write = [&](const u32x4_t* rr, int buf) {
+            char* dst = vt[buf][grp] + n * TL::VTST + 16 * hb;
 #pragma unroll
-            for (int sub = 0; sub < SUB; ++sub) {
-                pf_store_k<D, KV>(rk[st][sub], kt[buf][sub]);
-                pf_store_v<D, KV>(rv[st][sub], vt[buf][sub]);
-                if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) {
-                    ks_s[buf][sub][threadIdx.x] = rks[st][sub];
-                    vs_s[buf][sub][threadIdx.x] = rvs[st][sub];
-                }
+            for (int u = 0; u < NTU; ++u) {
+                const int cc = 4 * u + (w & 3);
+                if (cc < NB * 2) *(u32x4_t*)(dst + (cc >> 1) * 32 * TL::VTST + 32 * (cc & 1)) = rr[u];
             }
         };
+        f32x16_t sacc[SUB];                      // S of a stage, from its multiply to its softmax
+        f16x8_t p[SUB][2];                       // P of a stage, from its softmax to the next multiply
 #pragma unroll
-        for (int u = 0; u < NST; ++u) load(u, u);
-        store(0, 0);
+        for (int sub = 0; sub < SUB; ++sub) {
+            sacc[sub] = f32x16_t{};
+            p[sub][0] = f16x8_t{};
+            p[sub][1] = f16x8_t{};
+        }
+        load(0);
+        store(0);
         __syncthreads();
-        for (int64_t base = 0; base < nstages; base += NST) {
-#pragma unroll
-            for (int u = 0; u < NST; ++u) {
-                const int64_t stage = base + u;
-                if (stage >= nstages) break;
-                const int buf = (int)(stage & 1);
-                const int64_t k0 = stage * SK;
-                if (k0 <= t) {
-                    f32x16_t sacc[SUB];
-#pragma unroll
-                    for (int sub = 0; sub < SUB; ++sub) {
-                        sacc[sub] = f32x16_t{};
-#pragma unroll
-                        for (int s = 0; s < KS; ++s)
-                            sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                lds_row_operand<D>(kt[buf][sub], n, hb * (D / 16) + s), qop[s], sacc[sub], 0, 0, 0);
+        {
+            u32x4_t tr[NTU];
+            t_read(tr);
+            t_write(tr, 0);
+        }
+        load(1);
+        __syncthreads();
+        for (int h = 0; h < 2 * nstages + 2; ++h) {
+            const int e = h - grp;
+            const int m = e >> 1;
+            if (e >= 0 && (e & 1) == 0) {
+                // ---- multiply half of stage m ----
+                // the multiplying wave issues first on its SIMD (otherwise the older wave of the
+                // pair wins the arbitration whatever it runs, and the other group's MFMAs starve)
+                __builtin_amdgcn_s_setprio(2);
+                // One software-pipelined sequence of up to 32 MFMAs: item i < NPV is
+                // O^T[dv][head] += V^T . P^T for (blk, sub, ks) = i, item NPV + j is k-step j of
+                // S^T = K . Q^T; each item's LDS operand is read kPfAhead items ahead.
+                const bool do_pv = m >= 1 && m - 1 <= last;
+                const bool do_qk = m < nstages && m <= last;
+                constexpr int NPV = NB * SUB * 2, NQK = SUB * KS;
+                // V (A operand): 8 keys of dim 32 blk + n from the V^T tile; K (B operand): 8
+                // consecutive d of key row n
+                const char* vtbase = vt[(m + NBUF - 1) % NBUF][0] + n * TL::VTST + 16 * hb;
+                const char* kbase = kt[m % NBUF][0] + n * TL::KST + hb * (D / 16) * 16;
+                auto rd = [&](int i) -> u32x4_t {
+                    if (i < NPV) {
+                        const int blk = i % NB, sub = (i / NB) / 2, ks = (i / NB) % 2;
+                        return *(const u32x4_t*)(vtbase + sub * TL::VTB + blk * 32 * TL::VTST + 32 * ks);
                     }
-                    // logits x = s * sc (sc > 0); keys past t are masked in the stage holding t
-                    float x[16 * SUB];
+                    const int j = i - NPV, sub = j % SUB, st = j / SUB;
+                    return *(const u32x4_t*)(kbase + sub * TL::KB + 16 * st);
+                };
+                auto mma = [&](int it, const u32x4_t& op) {
+                    // consecutive items use different accumulators (dependent MFMAs would wait for
+                    // each other's results)
+                    if (it < NPV) {
+                        const int blk = it % NB, sub = (it / NB) / 2, ks = (it / NB) % 2;
+                        oacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(f16x8_t, op), p[sub][ks], oacc[blk], 0, 0, 0);
+                    } else {
+                        const int j = it - NPV, sub = j % SUB, st = j / SUB;
+                        sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8_t, op), qop[st], sacc[sub], 0, 0, 0);
+                    }
+                };
+                // items [I0, I1) as one static sequence; after item kPfMid the group stores its
+                // sub-tile of stage m + 1 and issues the loads of stage m + 2, and their vector and
+                // memory instructions are spread between the remaining MFMAs.  Stage m + 1's buffers
+                // are free at this point even past the last stage (the extra stores go unused).
+                auto seq = [&](auto pv, auto qk) {
+                    constexpr int I0 = decltype(pv)::value ? 0 : NPV;
+                    constexpr int I1 = decltype(qk)::value ? NPV + NQK : NPV;
+                    constexpr int N = I1 - I0;
+                    u32x4_t win[kPfAhead];
+                    // LDS instructions per item
+                    auto nrd = [](int) { return 1; };
+                    int pro = 0;
 #pragma unroll
-                    for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-                        for (int i = 0; i < 16; ++i) {
-                            const int kr = 8 * (i >> 2) + 4 * hb + (i & 3);    // key row in the sub-tile
-                            x[16 * sub + i] = KV == HS2_FP8_E4M3 ? sacc[sub][i] * (sl2 * ks_s[buf][sub][kr]) : sacc[sub][i];
+                    for (int i = 0; i < kPfAhead; ++i)
+                        if (i < N) {
+                            win[i] = rd(I0 + i);
+                            pro += nrd(I0 + i);
                         }
+                    if (decltype(qk)::value) {
+                        sacc[0] = f32x16_t{};
+                        sacc[1] = f32x16_t{};
+                    }
+                    constexpr int MID = N > kPfMid ? kPfMid : N - 1;
+#pragma unroll
+                    for (int i = 0; i < N; ++i) {
+                        const u32x4_t op = win[i % kPfAhead];
+                        if (i + kPfAhead < N) win[i % kPfAhead] = rd(I0 + i + kPfAhead);
+                        mma(I0 + i, op);
+                        if (i == MID) {
+                            store((m + 1) % NBUF);
+                            load(m + 2);
+                        }
+                    }
+                    // keep the order: the prologue reads, then per item its MFMA followed by the
+                    // reads of the item kPfAhead later
+#pragma unroll
+                    for (int r = 0; r < 2 * kPfAhead; ++r)
+                        if (r < pro) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+                    for (int i = 0; i < N; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+                        for (int r = 0; r < 2; ++r)
+                            if (i + kPfAhead < N && r < nrd(I0 + i + kPfAhead)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                        if (i > MID) {
+                            // after the store point: a few vector ALU ops, one LDS write and one
+                            // global load per MFMA while they last
+                            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                        }
+                    }
+                };
+                if (do_pv && do_qk) seq(std::true_type{}, std::true_type{});
+                else if (do_pv) seq(std::true_type{}, std::false_type{});
+                else if (do_qk) seq(std::false_type{}, std::true_type{});
+                else {
+                    store((m + 1) % NBUF);
+                    load(m + 2);
+                }
+            } else if (e >= 0) {
+                // ---- softmax half of stage m: first the group's V^T of stage m + 1 ----
+                u32x4_t tr[NTU];
+                if (m + 1 < nstages) t_read(tr);
+                if (m < nstages && m <= last) {
+                    const int kb = m % NBUF;
+                    const int64_t k0 = (int64_t)m * SK;
+                    // logits x = s * sc (sc > 0), in place in the accumulators (a copy would cost
+                    // a move per value); keys past t are masked in the stage holding t
+                    if (KV == HS2_FP8_E4M3) {
+#pragma unroll
+                        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i)
+                                sacc[sub][i] *= sl2 * ks_s[kb][sub][8 * (i >> 2) + 4 * hb + (i & 3)];
+                    }
                     if (k0 + SK - 1 > t) {
                         const int lim = (int)(t - k0);
 #pragma unroll
                         for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
                             for (int i = 0; i < 16; ++i)
-                                if (kTileRows * sub + 8 * (i >> 2) + 4 * hb + (i & 3) > lim) x[16 * sub + i] = kNegInf;
+                                if (kTileRows * sub + 8 * (i >> 2) + 4 * hb + (i & 3) > lim) sacc[sub][i] = kNegInf;
                     }
-                    float mt = x[0];
-#pragma unroll
-                    for (int i = 1; i < 16 * SUB; ++i) mt = fmaxf(mt, x[i]);
-                    mt = pf_half_max(mt);
-                    // bf16 path: x is still unscaled, scale the maximum (sc > 0 keeps the order)
+                    // bf16 path: x is still unscaled, sc is applied inside the exponent
                     const float scl = KV == HS2_FP8_E4M3 ? 1.f : sl2;
-                    const float mn = fmaxf(m_run, mt * scl);
-                    const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_run - mn);
-                    const float mref = (mn == kNegInf) ? 0.f : mn;
-                    float ps = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16 * SUB; ++i) {
-                        x[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scl, -mref));
-                        ps += x[i];
-                    }
-                    l_run = l_run * alpha + ps;
-                    m_run = mn;
-                    if (KV == HS2_FP8_E4M3) {
+                    // weights 2^(x - mr) into the fp16 P operand (times the V row scale for FP8);
+                    // returns the lane's fp32 sum of the unscaled weights (l feeds the log-sum-exp
+                    // of the selection scores, which needs more than fp16 precision)
+                    auto weights = [&](float mr) -> float {
+                        float ps = 0.f;
 #pragma unroll
                         for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) x[16 * sub + i] *= vs_s[buf][sub][8 * (i >> 2) + 4 * hb + (i & 3)];
+                            for (int i = 0; i < 16; ++i) {
+                                float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][i], scl, -mr));
+                                ps += e2;
+                                if (KV == HS2_FP8_E4M3) e2 *= vs_s[kb][sub][8 * (i >> 2) + 4 * hb + (i & 3)];
+                                p[sub][i >> 3][i & 7] = (_Float16)e2;
+                            }
+                        return ps;
+                    };
+                    // the reference stays while every lane's weights sum to at most kPfWeightMax;
+                    // otherwise (and on the wave's first stage) it moves to the running maximum
+                    // and O and l are rescaled
+                    bool slow = m_ref == kNegInf;
+                    float ps = 0.f;
+                    if (!__builtin_amdgcn_ballot_w64(slow)) {
+                        ps = weights(m_ref);
+                        slow = !(ps <= kPfWeightMax);    // also catches an overflow to inf
                     }
-                    if (__ballot(alpha != 1.f)) {
+                    if (__builtin_amdgcn_ballot_w64(slow)) {
+                        float mt = sacc[0][0];
+#pragma unroll
+                        for (int sub = 0; sub < SUB; ++sub)
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[sub][i]);
+                        const float mn = fmaxf(m_ref, pf_half_max(mt) * scl);
+                        // exp2(-inf) = 0 clears nothing that is not already zero on a head's
+                        // first stage; while a head has seen only masked keys (mn = -inf) the
+                        // reference point is 0, never -inf - (-inf)
+                        const float alpha = mn == kNegInf ? 1.f : __builtin_amdgcn_exp2f(m_ref - mn);
+                        m_ref = mn;
+                        l_run *= alpha;
 #pragma unroll
                         for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
                             for (int i = 0; i < 16; ++i) oacc[blk][i] *= alpha;
+                        ps = weights(mn == kNegInf ? 0.f : mn);
                     }
-                    f16x8_t p[SUB][2];
-#pragma unroll
-                    for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            p[sub][0][e] = (_Float16)x[16 * sub + e];
-                            p[sub][1][e] = (_Float16)x[16 * sub + 8 + e];
-                        }
-#pragma unroll
-                    for (int blk = 0; blk < NB; ++blk)
-#pragma unroll
-                        for (int sub = 0; sub < SUB; ++sub)
-#pragma unroll
-                            for (int ks = 0; ks < 2; ++ks)
-                                oacc[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                    lds_vt_operand_f16<D>(vt[buf][sub], blk, ks), p[sub][ks], oacc[blk], 0, 0, 0);
+                    l_run += ps;
                 }
-                // stage + 1 (registers (u+1) % NST) into the other buffer, refill registers u
-                if (stage + 1 < nstages) store((u + 1) % NST, buf ^ 1);
-                load(u, stage + NST);
-                __syncthreads();
+                if (m + 1 < nstages) t_write(tr, (m + 1) % NBUF);
             }
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     l_run = pf_half_sum(l_run);
@@ -341,7 +530,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                     v4.z = oacc[blk][4 * g + 2] * linv; v4.w = oacc[blk][4 * g + 3] * linv;
                     *(float4*)(po + n * D + dv) = v4;
                 }
-            if (hb == 0 && a.lse) a.lse[(int64_t)r * H + n] = l_run > 0.f ? m_run + log2f(l_run) : kNegInf;
+            if (hb == 0 && a.lse) a.lse[(int64_t)r * H + n] = l_run > 0.f ? m_ref + log2f(l_run) : kNegInf;
         }
     }
 }
@@ -350,7 +539,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
 template <int D, int KV>
 __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;
-    constexpr int NX = PfGeom<D, KV>::NX;
+    constexpr int NX = PfGeom<D, KV, kPfThreads>::NX;
     constexpr int NST = 4;
     __shared__ __attribute__((aligned(16))) char kt[2][LdsTile<D>::BYTES];
     __shared__ float ks_s[2][kTileRows];
@@ -388,7 +577,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
 
     if (ntiles > 0) {
         const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
-        const PfLoader<D, KV> ld;
+        const PfLoader<D, KV, kPfThreads> ld(threadIdx.x);
         u32x4_t rk[NST][NX];
         float rks[NST];
         auto load = [&](int st, int64_t tile) {
@@ -400,7 +589,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
             }
         };
         auto store = [&](int st, int buf) {
-            pf_store_k<D, KV>(rk[st], kt[buf]);
+            pf_store_k<D, KV, kPfThreads, 0>(rk[st], kt[buf], threadIdx.x);
             if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) ks_s[buf][threadIdx.x] = rks[st];
         };
 #pragma unroll
