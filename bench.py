@@ -2,7 +2,7 @@
 
 A step is one pass of the whole hot path over one batch: the full-attention MQA layer with
 token-level selection (hs2_full_attn_select) followed by the index-reusing sparse layers
-(hs2_sparse_attn), plus the KV bridge for the prefill-exit workload.  Inputs are resident in
+(hs2_sparse_attn_layers), plus the KV bridge for the prefill-exit workload.  Inputs are resident in
 HBM before the timed region.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode128k]
@@ -72,6 +72,8 @@ def algorithmic(cfg):
     out = {
         "full_attn": {"bytes": cfg.B * cfg.N * 2 * kvb, "flops": full_flops},
         "sparse_attn": {"bytes": sparse_bytes, "flops": sparse_flops},
+        # all sparse layers in one launch: each layer still gathers its rows
+        "sparse_layers": {"bytes": cfg.n_sparse * sparse_bytes, "flops": cfg.n_sparse * sparse_flops},
         "step": {"bytes": full_bytes + cfg.n_sparse * sparse_bytes,
                  "flops": full_flops + cfg.n_sparse * sparse_flops},
     }
@@ -90,12 +92,14 @@ KERNEL_UNITS = {
     "full_attn_prefill": ("full_attn", "mfma"),
     "sparse_attn_generic": ("sparse_attn", "hbm"),
     "sparse_attn_mfma": ("sparse_attn", "hbm"),
+    "sparse_attn_layers_mfma": ("sparse_layers", "hbm"),
     "bridge_mfma": ("bridge", "hbm"),
 }
 KERNEL_SOURCES = {
     "full_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "full_attn_prefill": ["attn_prefill.hip", "mfma_tiles.h"],
     "sparse_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
+    "sparse_attn_layers_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "bridge_mfma": ["bridge_mfma.hip", "mfma_tiles.h"],
 }
 
@@ -140,7 +144,7 @@ def run_gpu(cfg, steps, warmup, profile=True):
     kvd = hs2.dtype_code(t["k"])
     ws = torch.empty((hs2.hs2_full_attn_select_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global,
                                                                cfg.window, kvd),), dtype=torch.uint8, device=dev)
-    sws = hs2.sparse_attn_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, dev)
+    sws = hs2.sparse_attn_layers_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, cfg.n_sparse, dev)
     o = torch.empty((cfg.B, cfg.Tq, cfg.H, cfg.d), dtype=torch.float32, device=dev)
     idx = torch.empty((cfg.B, cfg.Tq, cfg.S), dtype=torch.int32, device=dev)
     o_sp = [torch.empty_like(o) for _ in range(cfg.n_sparse)]
@@ -151,9 +155,9 @@ def run_gpu(cfg, steps, warmup, profile=True):
         hs2.hs2_full_attn_select(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
                                  v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
                                  o=o, idx=idx, workspace=ws)
-        for l in range(cfg.n_sparse):
-            hs2.hs2_sparse_attn(t["qs"][l], t["k"], t["v"], idx, kv_len=t["kv_len"], k_scale=t["k_scale"],
-                                v_scale=t["v_scale"], sm_scale=sm, o=o_sp[l], workspace=sws)
+        # the sparse layers share the K/V cache and the indices: one call (one launch per kernel)
+        hs2.hs2_sparse_attn_layers(t["qs"], t["k"], t["v"], idx, kv_len=t["kv_len"], k_scale=t["k_scale"],
+                                   v_scale=t["v_scale"], sm_scale=sm, os=o_sp, workspace=sws)
 
     log(f"[bench] warmup {warmup}")
     for _ in range(warmup):

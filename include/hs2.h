@@ -147,6 +147,29 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype,
  */
 size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S);
 
+/*
+ * L sparse layers of one hybrid block in one call: every layer reuses the same KV cache and
+ * index lists with its own queries (KV Reuse: lynxflow "Two-Level KV Sharing"; agentik-os
+ * section 2, where several sparse layers follow one full layer).  Layer l computes exactly
+ * what hs2_sparse_attn computes for q[l] into o[l]; on the MFMA paths all layers share one
+ * launch of each kernel (the per-layer launches are what bound decode-sized sparse layers).
+ * q, o: HOST arrays of L device pointers ([B, Tq, H, d] each); 1 <= L <= 8.
+ * workspace (optional): hs2_sparse_attn_layers_workspace_size bytes (L times the per-layer
+ * size); with a smaller one every row is handled by one workgroup per layer.
+ * Other arguments, requirements and errors as for hs2_sparse_attn.
+ */
+hs2_status hs2_sparse_attn_layers(const void* const* q, int32_t L, hs2_dtype q_dtype,
+                                  const void* k, const void* v, hs2_dtype kv_dtype,
+                                  const float* k_scale, const float* v_scale,
+                                  const int32_t* idx, int32_t S, const int32_t* kv_len,
+                                  int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                  float sm_scale, float* const* o,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes for hs2_sparse_attn_layers with L layers (0 if L is outside [1, 8]). */
+size_t hs2_sparse_attn_layers_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S,
+                                             int32_t L);
+
 /* Thread-local message describing the last non-OK status returned on this thread. */
 const char* hs2_last_error(void);
 

@@ -101,6 +101,41 @@ def test_sparse_rejects(kw, status):
     assert _sp(**kw) == status
 
 
+def _spl(L=3, qarr=True, oarr=True, **kw):
+    a = dict(qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, idx=FAKE, S=1152,
+             kl=None, B=1, Tq=1, H=32, d=128, N=4096, sm=0.088, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    n = max(L, 1)
+    qa = ctypes.cast((ctypes.c_void_p * n)(*([kw.get("q", FAKE)] * n)), ctypes.c_void_p) if qarr else None
+    oa = ctypes.cast((ctypes.c_void_p * n)(*([kw.get("o", FAKE)] * n)), ctypes.c_void_p) if oarr else None
+    return hs2.lib().hs2_sparse_attn_layers(qa, L, a["qd"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"], a["idx"],
+                                            a["S"], a["kl"], a["B"], a["Tq"], a["H"], a["d"], a["N"], a["sm"], oa,
+                                            a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(L=9), hs2.HS2_ERR_INVALID_ARG),
+    (dict(qarr=False), hs2.HS2_ERR_INVALID_ARG),
+    (dict(oarr=False), hs2.HS2_ERR_INVALID_ARG),
+    (dict(q=None), hs2.HS2_ERR_INVALID_ARG),          # a null layer query
+    (dict(o=None), hs2.HS2_ERR_INVALID_ARG),          # a null layer output
+    (dict(S=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(d=32), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(B=0), hs2.HS2_OK),                          # empty batch: nothing launched
+])
+def test_sparse_layers_rejects(kw, status):
+    assert _spl(**kw) == status
+
+
+def test_sparse_layers_workspace_size():
+    one = hs2.hs2_sparse_attn_workspace_size(8, 1, 32, 128, 1152)
+    assert one > 0
+    assert hs2.hs2_sparse_attn_layers_workspace_size(8, 1, 32, 128, 1152, 3) == 3 * one
+    assert hs2.hs2_sparse_attn_layers_workspace_size(8, 1, 32, 128, 1152, 0) == 0
+    assert hs2.hs2_sparse_attn_layers_workspace_size(8, 1, 32, 128, 1152, 9) == 0
+
+
 @pytest.mark.parametrize("args,status", [
     ((FAKE, 10, 100, FAKE, FAKE, 128, FAKE, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),   # D % 64
     ((FAKE, 10, 128, FAKE, FAKE, 96, FAKE, FAKE, 128, None), hs2.HS2_ERR_UNSUPPORTED),

@@ -139,6 +139,26 @@ def test_sparse_workspace_reuse():
             assert torch.equal(ref, got), f"{cfg.name} pass {rep}: reused workspace changed the result"
 
 
+@pytest.mark.parametrize("kv,B,Tq", [("bf16", 4, 2), ("fp8", 4, 2), ("bf16", 1, 16)])
+def test_sparse_layers_match_per_layer(kv, B, Tq):
+    """hs2_sparse_attn_layers gives every layer the same bytes as hs2_sparse_attn on that layer
+    (same split plan and kernels, all layers in one launch), with and without a workspace."""
+    import token_level_sparse_mqa_amd as hs2
+    cfg = small_config(f"layers_{kv}_{B}x{Tq}", 232 + (kv == "fp8") + 2 * (Tq > 8), B=B, N=3000, Tq=Tq,
+                       n_sparse=3, kv_dtype=kv)
+    _say(f"[layers] {cfg.name}")
+    g = GpuRun(make_workload(cfg))
+    _, idx, _ = g.full()
+    for ws_on in (True, False):
+        refs = [g.sparse(layer, idx, workspace=ws_on) for layer in range(3)]
+        ws = hs2.sparse_attn_layers_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, 3, "cuda") if ws_on else None
+        got = hs2.hs2_sparse_attn_layers(g.qs, g.k, g.v, idx, kv_len=g.kv_len, k_scale=g.k_scale,
+                                         v_scale=g.v_scale, sm_scale=g.sm, workspace=ws)
+        torch.cuda.synchronize()
+        for layer in range(3):
+            assert torch.equal(refs[layer], got[layer]), f"layer {layer} workspace={ws_on}"
+
+
 def test_empty_batch_is_noop():
     import token_level_sparse_mqa_amd as hs2
     q = torch.empty((0, 1, 32, 128), dtype=torch.bfloat16, device="cuda")

@@ -5,7 +5,8 @@ called through its C ABI (include/hs2.h) with ctypes.  torch provides device mem
 the current stream.  The functions carry the C names:
 
     hs2_kv_bridge, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
-    hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_last_error, hs2_version
+    hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_sparse_attn_layers,
+    hs2_sparse_attn_layers_workspace_size, hs2_last_error, hs2_version
 
 There is no fallback: if the built library is missing, loading raises.
 """
@@ -35,6 +36,10 @@ _SIGS = {
     "hs2_sparse_attn": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _vp,
                                        _i32, _i32, _i32, _i32, _i64, _f32, _vp, _vp, _sz, _vp]),
     "hs2_sparse_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "hs2_sparse_attn_layers": (ctypes.c_int, [_vp, _i32, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                              _i32, _vp, _i32, _i32, _i32, _i32, _i64, _f32, _vp, _vp, _sz,
+                                              _vp]),
+    "hs2_sparse_attn_layers_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "hs2_last_error": (ctypes.c_char_p, []),
     "hs2_version": (ctypes.c_char_p, []),
     "hs2_profile_enable": (None, [ctypes.c_int]),
@@ -181,6 +186,43 @@ def hs2_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torc
         _ptr(q), dtype_code(q), _ptr(k), _ptr(v), dtype_code(k), _ptr(k_scale), _ptr(v_scale), _ptr(idx), S,
         _ptr(kv_len), B, Tq, H, d, Nmax, float(sm_scale), _ptr(o), _ptr(workspace), wsb, _stream(stream)))
     return o
+
+
+def hs2_sparse_attn_layers_workspace_size(B: int, Tq: int, H: int, d: int, S: int, L: int) -> int:
+    return int(lib().hs2_sparse_attn_layers_workspace_size(B, Tq, H, d, S, L))
+
+
+def sparse_attn_layers_workspace(B: int, Tq: int, H: int, d: int, S: int, L: int, device) -> torch.Tensor:
+    """A workspace for hs2_sparse_attn_layers with L layers (reusable across ordered calls)."""
+    n = hs2_sparse_attn_layers_workspace_size(B, Tq, H, d, S, L)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device)
+
+
+def hs2_sparse_attn_layers(qs, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                           kv_len: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
+                           v_scale: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
+                           os=None, workspace: Optional[torch.Tensor] = None, stream=None):
+    """L sparse layers (one query tensor each) over the same KV and indices in one call.
+    Returns the list of o tensors (fp32 [B,Tq,H,d])."""
+    L = len(qs)
+    B, Tq, H, d = qs[0].shape
+    for q in qs:
+        if q.shape != qs[0].shape or q.dtype != qs[0].dtype:
+            raise ValueError("all layers' queries must have the same shape and dtype")
+    Nmax = k.shape[1]
+    S = idx.shape[-1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if os is None:
+        os = [torch.empty((B, Tq, H, d), dtype=torch.float32, device=qs[0].device) for _ in range(L)]
+    qa = (ctypes.c_void_p * L)(*[_ptr(q) for q in qs])
+    oa = (ctypes.c_void_p * L)(*[_ptr(o) for o in os])
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().hs2_sparse_attn_layers(
+        ctypes.cast(qa, ctypes.c_void_p), L, dtype_code(qs[0]), _ptr(k), _ptr(v), dtype_code(k), _ptr(k_scale),
+        _ptr(v_scale), _ptr(idx), S, _ptr(kv_len), B, Tq, H, d, Nmax, float(sm_scale),
+        ctypes.cast(oa, ctypes.c_void_p), _ptr(workspace), wsb, _stream(stream)))
+    return os
 
 
 def profile_enable(enable: bool = True):

@@ -309,17 +309,36 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
                            const float* k_scale, const float* v_scale, const int32_t* idx, int32_t S,
                            const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
                            float sm_scale, float* o, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
-    if (st != HS2_OK) return st;
+    return hs2_sparse_attn_layers(&q, 1, q_dtype, k, v, kv_dtype, k_scale, v_scale, idx, S, kv_len, B, Tq, H, d,
+                                  Nmax, sm_scale, &o, workspace, workspace_bytes, stream);
+}
+
+size_t hs2_sparse_attn_layers_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S, int32_t L) {
+    if (L < 1 || L > kMaxLayers) return 0;
+    const size_t n = hs2_sparse_attn_workspace_size(B, Tq, H, d, S);
+    return n ? n * (size_t)L : 0;
+}
+
+hs2_status hs2_sparse_attn_layers(const void* const* q, int32_t L, hs2_dtype q_dtype, const void* k, const void* v,
+                                  hs2_dtype kv_dtype, const float* k_scale, const float* v_scale, const int32_t* idx,
+                                  int32_t S, const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d,
+                                  int64_t Nmax, float sm_scale, float* const* o, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+    if (!q || !o) return fail(HS2_ERR_INVALID_ARG, "null q or o pointer array");
+    if (L < 1 || L > kMaxLayers) return fail(HS2_ERR_INVALID_ARG, "L=%d outside [1, %d]", L, kMaxLayers);
+    for (int l = 0; l < L; ++l) {
+        hs2_status st = check_common(q[l], q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o[l]);
+        if (st != HS2_OK) return st;
+    }
     if (S < 1 || S > 8192) return fail(HS2_ERR_INVALID_ARG, "S=%d outside [1, 8192]", S);
     if ((int64_t)B * Tq == 0) return HS2_OK;
     if (!idx) return fail(HS2_ERR_INVALID_ARG, "null idx pointer");
     const int64_t R = (int64_t)B * Tq;
-    const size_t need = sparse_ws_bytes(R, H, d, S, q_dtype);
-    const bool split = workspace && need > 0 && workspace_bytes >= need;
+    const size_t need = sparse_ws_bytes(R, H, d, S, q_dtype);        // per layer
+    const bool split = workspace && need > 0 && workspace_bytes >= need * (size_t)L;
 
     AttnArgs aa{};
-    aa.q = q; aa.q_dtype = q_dtype; aa.k = k; aa.v = v; aa.kv_dtype = kv_dtype;
+    aa.q = q[0]; aa.q_dtype = q_dtype; aa.k = k; aa.v = v; aa.kv_dtype = kv_dtype;
     aa.k_scale = k_scale; aa.v_scale = v_scale; aa.q_pos = nullptr; aa.kv_len = kv_len;
     aa.list = idx; aa.S = S; aa.B = B; aa.Tq = Tq; aa.H = H; aa.d = d; aa.Nmax = Nmax;
     aa.scale_log2 = sm_scale * 1.4426950408889634f;
@@ -332,19 +351,36 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype, const void* k, cons
     // the MFMA kernel stages at most 1280 list entries per workgroup; longer unsplit lists
     // take the generic kernel
     const bool mfma = q_dtype != HS2_F32 && aa.chunk <= 1280;
-    aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
-    aa.part_ml = aa.part ? aa.part + R * aa.nsplit * H * d : nullptr;   // MFMA layout
-    aa.o = o; aa.lse = nullptr;
     hipError_t e;
     if (!mfma) {
-        e = launch_attn_generic(aa, "sparse_attn_generic", stream);
-        if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
-        if (aa.nsplit > 1) e = launch_attn_combine(aa, "sparse_attn_combine", stream);
-    } else {
-        e = launch_attn_rows_mfma(aa, "sparse_attn_mfma", stream);
-        if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
-        if (aa.nsplit > 1) e = launch_attn_split_combine(aa, "sparse_attn_combine", stream);
+        // generic kernels: one layer per launch
+        for (int l = 0; l < L; ++l) {
+            aa.q = q[l];
+            aa.o = o[l];
+            aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
+            e = launch_attn_generic(aa, "sparse_attn_generic", stream);
+            if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+            if (aa.nsplit > 1) e = launch_attn_combine(aa, "sparse_attn_combine", stream);
+            if (e != hipSuccess) return hip_fail(e, "sparse combine launch");
+        }
+        return HS2_OK;
     }
+    // MFMA kernels: all layers in one launch of each kernel.  Partial results of layer l:
+    // o at part + l * R * nsplit * H * d, (m, l) at part_ml + l * R * nsplit * H * 2.
+    aa.nlayer = L;
+    for (int l = 0; l < L; ++l) {
+        aa.ql[l] = q[l];
+        aa.ol[l] = o[l];
+    }
+    aa.o = o[0];
+    aa.lse = nullptr;
+    aa.part_lstride = R * aa.nsplit * H * d;
+    aa.ml_lstride = R * aa.nsplit * H * 2;
+    aa.part = aa.nsplit > 1 ? (float*)workspace : nullptr;
+    aa.part_ml = aa.part ? aa.part + L * aa.part_lstride : nullptr;
+    e = launch_attn_rows_mfma(aa, L > 1 ? "sparse_attn_layers_mfma" : "sparse_attn_mfma", stream);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    if (aa.nsplit > 1) e = launch_attn_split_combine(aa, L > 1 ? "sparse_attn_layers_combine" : "sparse_attn_combine", stream);
     if (e != hipSuccess) return hip_fail(e, "sparse combine launch");
     return HS2_OK;
 }

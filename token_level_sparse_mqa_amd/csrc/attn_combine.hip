@@ -7,6 +7,28 @@ namespace hs2 {
 
 constexpr int kCombineNarrowMax = 32;  // splits up to which a (row, head) workgroup merges alone
 
+// The row of a workgroup and its buffers (multi-layer launches: block row x is row x % R of
+// layer x / R).
+struct CombineRow {
+    int r;
+    const float* part;
+    const float* part_ml;
+    float* o;
+    float* lse;
+};
+__device__ __forceinline__ CombineRow combine_row(const AttnArgs& a) {
+    CombineRow c{(int)blockIdx.x, a.part, a.part_ml, a.o, a.lse};
+    if (a.nlayer > 1) {
+        const int R = a.B * a.Tq, layer = c.r / R;
+        c.r -= layer * R;
+        c.part += layer * a.part_lstride;
+        c.part_ml += layer * a.ml_lstride;
+        c.o = a.ol[layer];
+        c.lse = nullptr;
+    }
+    return c;
+}
+
 // ---- merge of the splits of each row ----------------------------------------------------------------
 // Many splits (long rows): grid (row, head, D/16), 256 threads = 16 dims x 16 split lanes.  Every
 // workgroup first reduces the per-split maxima and sums of its head (tiny), then sums its 16
@@ -15,11 +37,12 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_split_combine_wide_kernel(AttnArgs a) {
     __shared__ float red[16][17];
     __shared__ float wred[4];
-    const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
+    const CombineRow cr = combine_row(a);
+    const int r = cr.r, h = blockIdx.y, H = a.H, ns = a.nsplit;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     // split s: o at obase + s * ostride, (m, l) at mbase + s * mstride
-    const float* obase = a.part + ((int64_t)r * ns * H + h) * D;
-    const float* mbase = a.part_ml + ((int64_t)r * ns * H + h) * 2;
+    const float* obase = cr.part + ((int64_t)r * ns * H + h) * D;
+    const float* mbase = cr.part_ml + ((int64_t)r * ns * H + h) * 2;
     const int64_t ostride = (int64_t)H * D, mstride = (int64_t)H * 2;
     float m = kNegInf;
     for (int s = tid; s < ns; s += 256) m = fmaxf(m, mbase[s * mstride]);
@@ -63,8 +86,8 @@ __global__ __launch_bounds__(256) void attn_split_combine_wide_kernel(AttnArgs a
 #pragma unroll
         for (int q = 0; q < 16; ++q) tot += red[q][tid];
         const int dvo = blockIdx.z * 16 + tid;
-        a.o[((int64_t)r * H + h) * D + dvo] = Ltot > 0.f ? tot / Ltot : 0.f;
-        if (dvo == 0 && a.lse) a.lse[(int64_t)r * H + h] = Ltot > 0.f ? M + log2f(Ltot) : kNegInf;
+        cr.o[((int64_t)r * H + h) * D + dvo] = Ltot > 0.f ? tot / Ltot : 0.f;
+        if (dvo == 0 && cr.lse) cr.lse[(int64_t)r * H + h] = Ltot > 0.f ? M + log2f(Ltot) : kNegInf;
     }
 }
 
@@ -74,10 +97,11 @@ __global__ __launch_bounds__(256) void attn_split_combine_wide_kernel(AttnArgs a
 template <int D>
 __global__ __launch_bounds__(D) void attn_split_combine_kernel(AttnArgs a) {
     constexpr int BATCH = 16;
-    const int r = blockIdx.x, h = blockIdx.y, H = a.H, ns = a.nsplit;
+    const CombineRow cr = combine_row(a);
+    const int r = cr.r, h = blockIdx.y, H = a.H, ns = a.nsplit;
     const int dv = threadIdx.x;
-    const float* obase = a.part + ((int64_t)r * ns * H + h) * D + dv;     // split s at + s * H * D
-    const float* mbase = a.part_ml + ((int64_t)r * ns * H + h) * 2;      // split s at + s * H * 2
+    const float* obase = cr.part + ((int64_t)r * ns * H + h) * D + dv;     // split s at + s * H * D
+    const float* mbase = cr.part_ml + ((int64_t)r * ns * H + h) * 2;      // split s at + s * H * 2
     float M = kNegInf, L = 0.f, acc = 0.f;
     for (int s0 = 0; s0 < ns; s0 += BATCH) {
         float2 ml[BATCH];
@@ -106,19 +130,19 @@ __global__ __launch_bounds__(D) void attn_split_combine_kernel(AttnArgs a) {
         }
         M = Mn;
     }
-    a.o[((int64_t)r * H + h) * D + dv] = L > 0.f ? acc / L : 0.f;
-    if (dv == 0 && a.lse) a.lse[(int64_t)r * H + h] = L > 0.f ? M + log2f(L) : kNegInf;
+    cr.o[((int64_t)r * H + h) * D + dv] = L > 0.f ? acc / L : 0.f;
+    if (dv == 0 && cr.lse) cr.lse[(int64_t)r * H + h] = L > 0.f ? M + log2f(L) : kNegInf;
 }
 
 // ---- launcher ------------------------------------------------------------------------------------
 hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s) {
     ProfScope ps(name, s);
     if (a.nsplit > kCombineNarrowMax) {
-        dim3 grid(a.B * a.Tq, a.H, a.d / 16);
+        dim3 grid(a.B * a.Tq * (a.nlayer > 1 ? a.nlayer : 1), a.H, a.d / 16);
         if (a.d == 128) attn_split_combine_wide_kernel<128><<<grid, 256, 0, s>>>(a);
         else attn_split_combine_wide_kernel<64><<<grid, 256, 0, s>>>(a);
     } else {
-        dim3 grid(a.B * a.Tq, a.H);
+        dim3 grid(a.B * a.Tq * (a.nlayer > 1 ? a.nlayer : 1), a.H);
         if (a.d == 128) attn_split_combine_kernel<128><<<grid, 128, 0, s>>>(a);
         else attn_split_combine_kernel<64><<<grid, 64, 0, s>>>(a);
     }

@@ -187,7 +187,22 @@ void attn_rows_mfma_kernel(AttnArgs a) {
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int n = lane & 31, hb = lane >> 5;
-    const int r = blockIdx.x, split = blockIdx.y;
+    int r = blockIdx.x;
+    const int split = blockIdx.y;
+    const void* qsrc = a.q;
+    float* odst = a.o;
+    float* part = a.part;
+    float* part_ml = a.part_ml;
+    if (a.nlayer > 1) {
+        const int R = a.B * a.Tq, layer = r / R;
+        r -= layer * R;
+        qsrc = a.ql[layer];
+        odst = a.ol[layer];
+        if (part) {
+            part += layer * a.part_lstride;
+            part_ml += layer * a.ml_lstride;
+        }
+    }
     const int b = r / a.Tq;
     const int H = a.H;
     const int64_t L = seq_len(a.kv_len, b, a.Nmax);
@@ -212,7 +227,7 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     }
     // Q (heads padded to 32 with zeros) as an LDS tile: the Q^T operand of every MFMA step
     {
-        const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)a.q + (int64_t)r * H * D);
+        const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)qsrc + (int64_t)r * H * D);
         constexpr int CPR = LdsTile<D>::CPR;
         for (int x = threadIdx.x; x < 32 * CPR; x += NT) {
             const int h = x / CPR, c = x % CPR;
@@ -283,7 +298,7 @@ void attn_rows_mfma_kernel(AttnArgs a) {
             }
     }
     __syncthreads();
-    const bool o_vec = ((uintptr_t)a.o & 15) == 0;
+    const bool o_vec = ((uintptr_t)odst & 15) == 0;
     for (int f = threadIdx.x; f < H * QN; f += NT) {
         const int h = f / QN, q = f % QN;
         const int slot = h * QN + (q ^ (h & (QN - 1)));
@@ -293,12 +308,12 @@ void attn_rows_mfma_kernel(AttnArgs a) {
             const float4 v = ((const float4*)&wl_s[ww])[slot];
             sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
         }
-        if (a.part) {
-            *(float4*)(a.part + (((int64_t)r * a.nsplit + split) * H + h) * D + 4 * q) = sum;
+        if (part) {
+            *(float4*)(part + (((int64_t)r * a.nsplit + split) * H + h) * D + 4 * q) = sum;
         } else {
             const float Lh = mlf_s[h][1];
             const float inv = Lh > 0.f ? 1.f / Lh : 0.f;
-            float* op = a.o + ((int64_t)r * H + h) * D + 4 * q;
+            float* op = odst + ((int64_t)r * H + h) * D + 4 * q;
             if (o_vec) {
                 *(float4*)op = make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
             } else {
@@ -308,8 +323,8 @@ void attn_rows_mfma_kernel(AttnArgs a) {
     }
     if (threadIdx.x < H) {
         const float Mh = mlf_s[threadIdx.x][0], Lh = mlf_s[threadIdx.x][1];
-        if (a.part)
-            *(float2*)(a.part_ml + (((int64_t)r * a.nsplit + split) * H + threadIdx.x) * 2) = make_float2(Mh, Lh);
+        if (part)
+            *(float2*)(part_ml + (((int64_t)r * a.nsplit + split) * H + threadIdx.x) * 2) = make_float2(Mh, Lh);
         else if (a.lse)
             a.lse[(int64_t)r * H + threadIdx.x] = Lh > 0.f ? Mh + log2f(Lh) : kNegInf;
     }
@@ -318,7 +333,7 @@ void attn_rows_mfma_kernel(AttnArgs a) {
 // ---- launcher ------------------------------------------------------------------------------------
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s) {
     ProfScope ps(name, s);
-    dim3 grid(a.B * a.Tq, a.nsplit);
+    dim3 grid(a.B * a.Tq * (a.nlayer > 1 ? a.nlayer : 1), a.nsplit);
     if (a.kv_dtype == HS2_FP8_E4M3) {
         if (a.d == 128) attn_rows_mfma_kernel<128, HS2_FP8_E4M3><<<grid, kRowWaves * 64, 0, s>>>(a);
         else attn_rows_mfma_kernel<64, HS2_FP8_E4M3><<<grid, kRowWaves * 64, 0, s>>>(a);

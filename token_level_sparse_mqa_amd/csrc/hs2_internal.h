@@ -19,6 +19,8 @@ constexpr int kSelSeg = 4096;
 
 // One attention problem: R = B*Tq query rows, each over a key set given either as the causal
 // range [0, t] (list == nullptr) or as an index list idx[r, 0:S].
+constexpr int kMaxLayers = 8;        // layers of one multi-layer sparse launch
+
 struct AttnArgs {
     const void* q; int q_dtype;          // [R, H, d]
     const void* k; const void* v; int kv_dtype;
@@ -37,6 +39,13 @@ struct AttnArgs {
     float* lse;                          // [R, H] base-2 log-sum-exp (nullptr: not needed)
     uint32_t* zero_hist;                 // [R, kHistBins] to clear (nullptr: none)
     uint32_t* zero_cnt;                  // [R, 4] to clear
+    // Several layers over the same K/V and index lists in one launch (nlayer > 1): block row x
+    // is row x % R of layer x / R, which takes its Q and O from ql / ol and its partial results
+    // at part + layer * part_lstride and part_ml + layer * ml_lstride.
+    int nlayer;
+    const void* ql[kMaxLayers];
+    float* ol[kMaxLayers];
+    int64_t part_lstride, ml_lstride;
 };
 
 struct ScoreArgs {
