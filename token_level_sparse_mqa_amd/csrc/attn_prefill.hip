@@ -536,13 +536,16 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
 }
 
 // ---- pass 2: selection scores ---------------------------------------------------------------------
+// 64-key stages (two 32-key sub-tiles) in three LDS buffers, software-pipelined per wave: the
+// MFMAs of stage m + 1 are issued before the exponentials of stage m, so the matrix cores and
+// the vector ALUs of a wave work at the same time.  One barrier per stage.
 template <int D, int KV>
 __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;
     constexpr int NX = PfGeom<D, KV, kPfThreads>::NX;
-    constexpr int NST = 4;
-    __shared__ __attribute__((aligned(16))) char kt[2][LdsTile<D>::BYTES];
-    __shared__ float ks_s[2][kTileRows];
+    constexpr int SUB = 2, SK = SUB * kTileRows, NBUF = 3;
+    __shared__ __attribute__((aligned(16))) char kt[NBUF][SUB][LdsTile<D>::BYTES];
+    __shared__ float ks_s[NBUF][SUB][kTileRows];
     __shared__ uint32_t hist[kPfWaves][kHistBins];
     __shared__ int64_t t_s[kPfWaves];
 
@@ -557,7 +560,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
     const int r = b * a.Tq + (live ? i0 + w : a.Tq - 1);
     const int64_t C = cand_count(t, a.window);
     const int64_t Cmax = cand_count(tmax, a.window);
-    const int64_t ntiles = (Cmax + kTileRows - 1) / kTileRows;
+    const int nstages = __builtin_amdgcn_readfirstlane((int)((Cmax + SK - 1) / SK));
+    const int last = __builtin_amdgcn_readfirstlane(C > 0 ? (int)((C - 1) / SK) : -1);   // last stage with candidates
     const int64_t rowbase = (int64_t)b * a.Nmax;
     for (int x = threadIdx.x; x < kPfWaves * kHistBins; x += kPfThreads) (&hist[0][0])[x] = 0;
 
@@ -575,56 +579,101 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
     }
     float* srow = a.scores + (int64_t)r * a.cstride;
 
-    if (ntiles > 0) {
+    if (nstages > 0) {
         const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
         const PfLoader<D, KV, kPfThreads> ld(threadIdx.x);
-        u32x4_t rk[NST][NX];
-        float rks[NST];
-        auto load = [&](int st, int64_t tile) {
-            const int64_t tl = tile < ntiles ? tile : ntiles - 1;
-            ld.load(rk[st], kseq, tl * kTileRows, Cmax);
-            if (KV == HS2_FP8_E4M3) {
-                const int64_t key = tl * kTileRows + (threadIdx.x & 31);
-                rks[st] = a.k_scale[rowbase + (key < Cmax ? key : Cmax - 1)];
-            }
-        };
-        auto store = [&](int st, int buf) {
-            pf_store_k<D, KV, kPfThreads, 0>(rk[st], kt[buf], threadIdx.x);
-            if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) ks_s[buf][threadIdx.x] = rks[st];
-        };
+        // two register stages: stage s is loaded into registers s % 2 two iterations before it
+        // is stored to LDS
+        u32x4_t rk[2][SUB][NX];
+        float rks[2][SUB];
+        auto load = [&](int stage) {
+            const int sg = stage < nstages ? stage : nstages - 1;
+            const int rs = stage & 1;
 #pragma unroll
-        for (int u = 0; u < NST; ++u) load(u, u);
-        store(0, 0);
-        __syncthreads();
-        for (int64_t base = 0; base < ntiles; base += NST) {
-#pragma unroll
-            for (int u = 0; u < NST; ++u) {
-                const int64_t tile = base + u;
-                if (tile >= ntiles) break;
-                const int buf = (int)(tile & 1);
-                const int64_t k0 = tile * kTileRows;
-                if (k0 < C) {
-                    f32x16_t sacc = f32x16_t{};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s)
-                        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], lds_row_operand<D>(kt[buf], n, hb * (D / 16) + s),
-                                                                       sacc, 0, 0, 0);
-                    float sc = a.scale_log2;
-                    if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][n];
-                    float acc = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sc, nlse[i]));
-                    acc += __shfl_xor(acc, 32);
-                    const int64_t j = k0 + n;
-                    if (hb == 0 && j < C) {
-                        srow[j] = acc;
-                        atomicAdd(&hist[w][__float_as_uint(acc) >> 21], 1u);
-                    }
+            for (int sub = 0; sub < SUB; ++sub) {
+                const int64_t k0 = (int64_t)sg * SK + sub * kTileRows;
+                ld.load_clamped(rk[rs][sub], kseq, k0, Cmax);
+                if (KV == HS2_FP8_E4M3) {
+                    const int64_t key = k0 + (threadIdx.x & 31);
+                    rks[rs][sub] = a.k_scale[rowbase + (key < Cmax ? key : Cmax - 1)];
                 }
-                if (tile + 1 < ntiles) store((u + 1) % NST, buf ^ 1);
-                load(u, tile + NST);
-                __syncthreads();
             }
+        };
+        auto store = [&](int stage) {
+            const int buf = stage % NBUF, rs = stage & 1;
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                pf_store_k<D, KV, kPfThreads, 0>(rk[rs][sub], kt[buf][sub], threadIdx.x);
+                if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) ks_s[buf][sub][threadIdx.x] = rks[rs][sub];
+            }
+        };
+        // S = Q . K^T of a stage's sub-tiles: lane (key n, half hb) holds heads 8 (i / 4) + 4 hb + i % 4
+        auto mma = [&](f32x16_t* sacc, int buf) {
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                sacc[sub] = f32x16_t{};
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], lds_row_operand<D>(kt[buf][sub], n, hb * (D / 16) + s),
+                                                                        sacc[sub], 0, 0, 0);
+            }
+        };
+        // score(j) = sum_h 2^(x_h(j) - lse_h): 16 heads per lane, the partner lane's 16 through
+        // v_permlane32_swap
+        auto scores = [&](const f32x16_t* sacc, int buf, float* acc) {
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+                float sc = a.scale_log2;
+                if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][sub][n];
+                float x = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) x += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][i], sc, nlse[i]));
+                acc[sub] = pf_half_sum(x);
+            }
+        };
+        f32x16_t sa[SUB], sb[SUB];            // S of consecutive stages (even / odd)
+        load(0);
+        store(0);
+        if (nstages > 1) {
+            load(1);
+            store(1);
+        }
+        load(2);
+        load(3);
+        __syncthreads();
+        mma(sa, 0);
+        // iteration m: the scores of stage m and the MFMAs of stage m + 1 in one branch-free block
+        // (MFMAs past the last stage read a stale buffer and their results go unused), then the
+        // stores of stage m's scores, stage m + 2 into LDS and the loads of stage m + 4
+        auto iter = [&](int m, f32x16_t* cur, f32x16_t* nxt) {
+            float acc[SUB];
+            scores(cur, m % NBUF, acc);
+            mma(nxt, (m + 1) % NBUF);
+            // MFMA k-steps interleaved with the exponentials: LDS operand reads run two k-steps
+            // ahead, about six vector instructions between MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < SUB * KS; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (i + 2 < SUB * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            }
+            if (m <= last) {
+                // both lane halves hold both sums: lane (n, hb) stores key n of sub-tile hb
+                const float v = hb ? acc[1] : acc[0];
+                const int64_t j = (int64_t)m * SK + hb * kTileRows + n;
+                if (j < C) {
+                    srow[j] = v;
+                    atomicAdd(&hist[w][__float_as_uint(v) >> 21], 1u);
+                }
+            }
+            if (m + 2 < nstages) store(m + 2);
+            load(m + 4);
+            __syncthreads();
+        };
+        for (int m = 0; m < nstages; m += 2) {
+            iter(m, sa, sb);
+            if (m + 1 < nstages) iter(m + 1, sb, sa);
         }
     }
     // this workgroup owns its rows' histograms entirely
