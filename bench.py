@@ -190,6 +190,50 @@ def run_gpu(cfg, steps, warmup, profile=True):
     return {"ms_per_step": ms, "wall_s": wall, "rows": R, "kernels": kernels, "wl": wl}
 
 
+def gather_cold_sweep(reps=5):
+    """Supplementary, labelled measurement of the sparse-layer kernel on decode-shaped gathers
+    large enough to be bandwidth-dominated: B sequences x 1 query x S = 1152 selected rows (a
+    random sorted set per query) out of a 1 GiB bf16 K+V cache, with the L2 and the memory-side
+    cache flushed (a 512 MiB buffer written) before every repetition.  Median over reps."""
+    import torch
+
+    import token_level_sparse_mqa_amd as hs2
+    dev = torch.device("cuda:0")
+    H, d, S = 32, 128, 1152
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1152)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = []
+    for B, N in ((16, 131072), (64, 32768), (256, 8192)):      # B * N * 512 B = 1 GiB of K+V
+        k = torch.randn((B, N, d), generator=gen, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, N, d), generator=gen, device=dev).to(torch.bfloat16)
+        q = torch.randn((B, 1, H, d), generator=gen, device=dev).to(torch.bfloat16)
+        idx = torch.rand((B, N), generator=gen, device=dev).argsort(dim=1)[:, :S].sort(dim=1).values
+        idx = idx.to(torch.int32).reshape(B, 1, S).contiguous()
+        ws = hs2.sparse_attn_workspace(B, 1, H, d, S, dev)
+        o = torch.empty((B, 1, H, d), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            hs2.hs2_sparse_attn(q, k, v, idx, o=o, workspace=ws)
+        times = []
+        for r in range(reps):
+            flush.fill_(r & 0xFF)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            hs2.hs2_sparse_attn(q, k, v, idx, o=o, workspace=ws)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        us = sorted(times)[len(times) // 2]
+        nbytes = B * (S * 2 * d * 2 + S * 4 + H * d * 2 + H * d * 4)
+        out.append({"B": B, "cache_rows_per_seq": N, "S": S, "bytes": nbytes, "us": us,
+                    "GB/s": nbytes / us / 1e3, "frac": nbytes / us / 1e3 / HBM_PEAK_GBS})
+        del k, v, q, idx, ws, o
+    del flush
+    return {"label": "supplementary: sparse-layer kernel, cold cache, decode-shaped gathers from a "
+                     "1 GiB bf16 K+V cache (not the timed step)", "points": out}
+
+
 def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0):
     """The float64 oracle, as it stands, on a bounded sample of the same workload: whole query
     rows, each with the full layer, the selection and every sparse layer, including decoding
@@ -243,6 +287,8 @@ def main():
     ap.add_argument("--workload", default="decode128k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
+    ap.add_argument("--no-gather-sweep", action="store_true",
+                    help="skip the cold-cache gather sweep reported with the decode workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration runs)")
     args = ap.parse_args()
@@ -298,6 +344,9 @@ def main():
                    "sparse_layers": cfg.n_sparse, "bridge_D": cfg.bridge_D},
         "roofline": roof, "step_roofline_frac": step_frac, "kernels": kernels,
     }
+    if cfg.Tq == 1 and not args.no_gather_sweep and not args.no_profile:
+        log("[bench] cold-cache gather sweep")
+        out["gather_cold_sweep"] = gather_cold_sweep()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(cfg, res["wl"])
