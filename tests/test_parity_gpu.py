@@ -100,6 +100,9 @@ SMALL = [
     small_config("chunk_fp8", 216, B=1, N=3001, Tq=24, kv_dtype="fp8", n_sparse=1),
     small_config("chunk_ragged", 217, B=2, N=2000, Tq=13, n_sparse=1),
     small_config("chunk_k16_w4", 218, B=1, N=500, Tq=16, n_sparse=1, k_global=16, window=4),
+    # 128 query rows: the sparse layer takes the several-tiles-in-flight kernel (FP8 and d=64)
+    small_config("rows128_fp8", 219, B=2, N=2000, Tq=64, kv_dtype="fp8", n_sparse=1),
+    small_config("rows128_d64", 220, B=2, N=1500, Tq=64, H=16, d=64, n_sparse=1),
 ]
 
 

@@ -98,9 +98,14 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
     return p;
 }
 
+// Splits of a sparse layer: about 256 workgroups over its rows, at least 128 list entries each.
+// Decode launches (a few rows) reach the limit of 128 entries per split; batches large enough to
+// be bandwidth-sized get long chunks and few splits to merge (measured on cold 1152-row
+// gathers: 15% faster than planning for 1024 workgroups).  The plan depends on one layer's rows
+// only, so a multi-layer launch gives every layer the bytes a one-layer launch gives it.
 void sparse_plan(int64_t R, int S, int q_dtype, int* nsplit, int64_t* chunk) {
     if (q_dtype == HS2_F32) split_range(R, S, 2048, 64, 32, nsplit, chunk);
-    else split_range(R, S, 1024, 128, 128, nsplit, chunk);
+    else split_range(R, S, 256, 128, 128, nsplit, chunk);
 }
 
 size_t sparse_ws_bytes(int64_t R, int H, int d, int S, int q_dtype) {
