@@ -190,6 +190,175 @@ def run_gpu(cfg, steps, warmup, profile=True):
     return {"ms_per_step": ms, "wall_s": wall, "rows": R, "kernels": kernels, "wl": wl}
 
 
+def agentic_units(cfg):
+    """Algorithmic bytes / flops of one agentic step (every span of every round), per kernel family:
+    the prefill attention over the observation chunks, the decode attention of the action tokens, the
+    sparse layers of all spans, and the bridge of all new rows."""
+    kvb = 2 * cfg.d                       # one bf16 K or V row
+    qb = 2 * cfg.H * cfg.d
+    units = {"full_attn_prefill": {"bytes": 0.0, "flops": 0.0}, "full_attn_mfma": {"bytes": 0.0, "flops": 0.0},
+             "sparse_layers": {"bytes": 0.0, "flops": 0.0}, "bridge": {"bytes": 0.0, "flops": 0.0},
+             "prefill_launches": 0, "decode_launches": 0}
+    for (kind, p, T) in cfg.phases():
+        pairs = sum(p + i + 1 for i in range(T))
+        key = "full_attn_prefill" if kind == "obs" else "full_attn_mfma"
+        units[key]["bytes"] += (p + T) * 2 * kvb
+        units[key]["flops"] += 4.0 * cfg.H * cfg.d * pairs
+        units["prefill_launches" if kind == "obs" else "decode_launches"] += 1
+        units["sparse_layers"]["bytes"] += cfg.n_sparse * T * (cfg.S * 2 * kvb + cfg.S * 4 + qb + cfg.H * cfg.d * 4)
+        units["sparse_layers"]["flops"] += cfg.n_sparse * 4.0 * cfg.H * cfg.d * cfg.S * T
+        units["bridge"]["bytes"] += T * (cfg.D * 2 + 4 * cfg.d) + 4 * cfg.D * cfg.d
+        units["bridge"]["flops"] += 2.0 * T * cfg.D * 2 * cfg.d
+    return units
+
+
+def run_agentic(cfg, steps, warmup, profile=True):
+    """The multi-turn loop: a step rewinds the session to the initial trace and runs every round
+    (act decoded tokens, then one observation chunk), bridging each new token into the cache.  It is
+    timed twice: launched from Python, and replayed from one HIP graph captured from the same calls."""
+    import torch
+
+    import token_level_sparse_mqa_amd as hs2
+    from token_level_sparse_mqa_amd.agentic import AgenticSession
+    from workloads import make_agentic
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name}")
+    inp = make_agentic(cfg)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    hid, qf, qs = up(inp.hidden), up(inp.q_full), [up(x) for x in inp.q_sparse]
+    sess = AgenticSession(up(inp.wk), up(inp.wv), capacity=cfg.N_final, H=cfg.H, n_sparse=cfg.n_sparse,
+                          max_span=cfg.obs, k_global=cfg.k_global, window=cfg.window)
+    sess.bridge_prefix(hid[:cfg.N0])
+    spans = [(hid[p:p + T], qf[p - cfg.N0:p - cfg.N0 + T], [x[p - cfg.N0:p - cfg.N0 + T] for x in qs])
+             for (_, p, T) in cfg.phases()]
+
+    def step():
+        sess.reset(cfg.N0)
+        for (h, q, q_sp) in spans:
+            sess.append(h, q, q_sp)
+
+    log(f"[bench] warmup {warmup}")
+    for _ in range(max(warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+
+    def timed(fn, nsteps):
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(nsteps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / nsteps, time.perf_counter() - w0
+
+    log(f"[bench] timing {steps} eager steps")
+    ms_eager, _ = timed(step, steps)
+    log("[bench] capturing the step in a HIP graph")
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        step()                      # one more warm pass on the capture stream (no allocation left)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} graph replays")
+    ms_graph, wall = timed(graph.replay, steps)
+    kernels = {}
+    if profile:
+        log(f"[bench] per-kernel event timing, {steps} eager steps")
+        hs2.profile_enable(True)
+        timed(step, steps)
+        kernels = hs2.profile_read()
+        hs2.profile_enable(False)
+    return {"ms_per_step": ms_graph, "ms_eager": ms_eager, "wall_s": wall, "rows": cfg.n_new,
+            "kernels": kernels, "inp": inp, "steps": steps}
+
+
+def agentic_cpu_baseline(cfg, inp, budget_s=20.0):
+    """The oracle on a bounded sample of the agentic step: the trace's K/V are bridged first
+    (untimed, as on the GPU), then spans in loop order, each bridging its rows and running every
+    row's full layer, selection and sparse layers, until the budget is spent."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    sm = 1.0 / math.sqrt(cfg.d)
+    kb, vb = oracle.kv_bridge(inp.hidden[:cfg.N0], inp.wk, inp.wv)
+    K = np.empty((cfg.N_final, cfg.d))
+    V = np.empty((cfg.N_final, cfg.d))
+    K[:cfg.N0], V[:cfg.N0] = oracle.decode(kb, "bf16"), oracle.decode(vb, "bf16")
+    t0 = time.perf_counter()
+    done = 0
+    for (kind, p, T) in cfg.phases():
+        kb, vb = oracle.kv_bridge(inp.hidden[p:p + T], inp.wk, inp.wv)
+        K[p:p + T], V[p:p + T] = oracle.decode(kb, "bf16"), oracle.decode(vb, "bf16")
+        for i in range(T):
+            j = p - cfg.N0 + i
+            _, idx, _ = oracle.full_attn_select_row(oracle.decode(inp.q_full[j], "bf16"), K, V, p + i, sm,
+                                                    cfg.k_global, cfg.window)
+            for l in range(cfg.n_sparse):
+                oracle.sparse_attention_row(oracle.decode(inp.q_sparse[l][j], "bf16"), K, V, idx, sm)
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {done} new tokens of one {cfg.name} step in loop order (bridge of their rows, "
+                      f"full layer + selection + {cfg.n_sparse} sparse layers per token; the initial "
+                      f"{cfg.N0}-row trace bridged beforehand, untimed), {el:.1f} s"}
+
+
+def agentic_main(cfg, args):
+    res = run_agentic(cfg, args.steps, args.warmup, profile=not args.no_profile)
+    ms = res["ms_per_step"]
+    units = agentic_units(cfg)
+    kernels = {}
+    for name, (tot, n) in res["kernels"].items():
+        kernels[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+    roof = None
+    if "full_attn_prefill" in kernels:
+        k = kernels["full_attn_prefill"]
+        per_step_s = k["avg_us"] * k["launches"] / res["steps"] / 1e6
+        ach = units["full_attn_prefill"]["flops"] / per_step_s / 1e12
+        roof = {"bound": "mfma", "kernel": "full_attn_prefill", "achieved": ach, "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS,
+                "traffic": stored_traffic(cfg.name, "full_attn_prefill"),
+                "per": f"sum over the step's {units['prefill_launches']} observation chunks"}
+    n_act = cfg.turns * cfg.act
+    out = {
+        "metric": "agentic loop: new tokens/s (action decode + observation prefill over a growing context)",
+        "value": cfg.n_new / (ms / 1e3), "unit": "new tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "B": 1, "initial_context": cfg.N0, "final_context": cfg.N_final,
+                   "turns": cfg.turns, "action_tokens": cfg.act, "observation_tokens": cfg.obs, "H": cfg.H,
+                   "d": cfg.d, "bridge_D": cfg.D, "kv_dtype": "bf16", "k_global": cfg.k_global,
+                   "window": cfg.window, "sparse_layers": cfg.n_sparse, "launch": "hip graph replay"},
+        "ms_per_step_eager": res["ms_eager"],
+        "roofline": roof, "kernels": kernels,
+    }
+    out["config"]["action_tokens_per_step"] = n_act
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = agentic_cpu_baseline(cfg, res["inp"])
+    print(json.dumps(out), flush=True)
+
+
 def gather_cold_sweep(reps=5):
     """Supplementary, labelled measurement of the sparse-layer kernel on decode-shaped gathers
     large enough to be bandwidth-dominated: B sequences x 1 query x S = 1152 selected rows (a
@@ -299,7 +468,10 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    from workloads import CONFIGS
+    from workloads import AGENTIC, CONFIGS
+    if args.workload in AGENTIC:
+        agentic_main(AGENTIC[args.workload], args)
+        return
     cfg = CONFIGS[args.workload]
     if args.calib_copy_mib:
         import torch

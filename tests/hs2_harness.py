@@ -13,6 +13,7 @@ Protocol per query row:
 from __future__ import annotations
 
 import math
+import sys
 from typing import Dict, List, Optional, Tuple
 
 import numpy as np
@@ -22,6 +23,11 @@ import oracle
 from workloads import Workload
 
 BAND = 1e-6
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
 
 
 def tol_for(kv_dtype: str) -> float:
@@ -143,3 +149,23 @@ def check_indices(idx_gpu: np.ndarray, idx_o: np.ndarray, score_o: np.ndarray, t
     for p in needles:
         assert p in set(gs.tolist()), f"needle {p} not picked"
     return {"mismatch": int(diff.size // 2), "n": n}
+
+
+def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0):
+    """GPU bridge output vs the oracle's: the bit patterns may differ only where fp32 summation
+    can move the sum across a bf16 rounding boundary.  Bound per element (sampled rows):
+    |gpu - exact| <= D * 2^-24 * sum_i |h_i w_i| + one bf16 ulp of the exact value."""
+    import oracle
+    D = hidden.shape[1]
+    frac_k, frac_v = float(np.mean(kb != ko)), float(np.mean(vb != vo))
+    _say(f"[parity] bridge mismatch fraction K {frac_k:.2e} V {frac_v:.2e}")
+    assert frac_k < 1e-3 and frac_v < 1e-3
+    rows = np.random.default_rng(seed).choice(hidden.shape[0], size=min(sample, hidden.shape[0]), replace=False)
+    h = oracle.decode(hidden[rows], "bf16")
+    for w_bits, got in ((wk, kb), (wv, vb)):
+        w = oracle.decode(w_bits, "bf16")
+        exact = h @ w
+        mag = np.abs(h) @ np.abs(w)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
+        err = np.abs(oracle.decode(got[rows], "bf16") - exact)
+        assert np.all(err <= D * 2.0 ** -24 * mag + ulp)

@@ -11,15 +11,13 @@ import numpy as np
 import pytest
 import torch
 
-from tests.hs2_harness import GpuRun, OracleRun, check_indices, tol_for, to_dev, bits_from_dev
+from tests.hs2_harness import (GpuRun, OracleRun, _say, bits_from_dev, check_bridge, check_indices,
+                               to_dev, tol_for)
 from workloads import CONFIGS, make_workload, small_config
 
 pytestmark = pytest.mark.gpu
 
 
-def _say(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
 
 
 def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=1e-7):
@@ -260,23 +258,3 @@ def test_full_prefill_exit256k_sampled():
     # the bridge itself against the float64 projection
     kb, vb = bits_from_dev(g.k[0]), bits_from_dev(g.v[0])
     check_bridge(wl.hidden, wl.wk, wl.wv, kb, vb, O.k_bits, O.v_bits)
-
-
-def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0):
-    """GPU bridge output vs the oracle's: the bit patterns may differ only where fp32 summation
-    can move the sum across a bf16 rounding boundary.  Bound per element (sampled rows):
-    |gpu - exact| <= D * 2^-24 * sum_i |h_i w_i| + one bf16 ulp of the exact value."""
-    import oracle
-    D = hidden.shape[1]
-    frac_k, frac_v = float(np.mean(kb != ko)), float(np.mean(vb != vo))
-    _say(f"[parity] bridge mismatch fraction K {frac_k:.2e} V {frac_v:.2e}")
-    assert frac_k < 1e-3 and frac_v < 1e-3
-    rows = np.random.default_rng(seed).choice(hidden.shape[0], size=min(sample, hidden.shape[0]), replace=False)
-    h = oracle.decode(hidden[rows], "bf16")
-    for w_bits, got in ((wk, kb), (wv, vb)):
-        w = oracle.decode(w_bits, "bf16")
-        exact = h @ w
-        mag = np.abs(h) @ np.abs(w)
-        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
-        err = np.abs(oracle.decode(got[rows], "bf16") - exact)
-        assert np.all(err <= D * 2.0 ** -24 * mag + ulp)

@@ -60,3 +60,22 @@ def test_spread64_plan():
     from workloads.gen import _needle_plan
     plan = _needle_plan(big)
     assert plan[0] == (0, 65536 + 63, 0, 512) and plan[63] == (0, 65536 + 64 * 63 + 63, 31, 1024 * 63 + 512)
+
+
+def test_agentic_phases_and_inputs():
+    from workloads import AGENTIC, AgenticConfig, make_agentic
+    cfg = AgenticConfig("t", 102, N0=50, turns=2, act=3, obs=7, H=2, d=64, D=64, n_sparse=2)
+    ph = cfg.phases()
+    # rounds of act single-token spans then one obs chunk, contiguous from N0 to N_final
+    assert [k for (k, _, _) in ph] == ["act"] * 3 + ["obs"] + ["act"] * 3 + ["obs"]
+    pos = cfg.N0
+    for (kind, p, T) in ph:
+        assert p == pos and T == (1 if kind == "act" else cfg.obs)
+        pos += T
+    assert pos == cfg.N_final == 50 + 2 * 10 and cfg.n_new == 20
+    a, b = make_agentic(cfg), make_agentic(cfg)
+    assert a.hidden.shape == (70, 64) and a.q_full.shape == (20, 2, 64) and len(a.q_sparse) == 2
+    assert a.wk.shape == (64, 64) and np.array_equal(a.hidden, b.hidden)
+    assert not np.array_equal(a.q_sparse[0], a.q_sparse[1])
+    big = AGENTIC["agentic"]
+    assert big.N_final == 131200 and big.n_new == 4 * (32 + 4096)

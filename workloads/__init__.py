@@ -8,3 +8,4 @@ path consume the bytes produced here.
 """
 from .configs import CONFIGS, Config, get_config, small_config  # noqa: F401
 from .gen import Workload, make_workload  # noqa: F401
+from .agentic import AGENTIC, AgenticConfig, AgenticInputs, make_agentic  # noqa: F401
