@@ -94,6 +94,7 @@ KERNEL_UNITS = {
     "sparse_attn_mfma": ("sparse_attn", "hbm"),
     "sparse_attn_layers_mfma": ("sparse_layers", "hbm"),
     "bridge_mfma": ("bridge", "hbm"),
+    "bridge_rows": ("bridge", "hbm"),
 }
 KERNEL_SOURCES = {
     "full_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
@@ -101,6 +102,7 @@ KERNEL_SOURCES = {
     "sparse_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "sparse_attn_layers_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "bridge_mfma": ["bridge_mfma.hip", "mfma_tiles.h"],
+    "bridge_rows": ["bridge_rows.hip"],
 }
 
 

@@ -35,6 +35,9 @@
  *    Kernels never read outside [0, Nmax) rows for them: a query whose position is outside
  *    [0, min(kv_len, Nmax)) produces o = 0 and an all -1 index row; index entries outside
  *    [0, min(kv_len, Nmax)) are skipped like -1.
+ *  - Alignment: q, k, v, o, hidden, w_k, w_v and the workspaces start on 16-byte boundaries;
+ *    the int32 and fp32 arrays (q_pos, kv_len, idx, scores, k_scale, v_scale) on 4-byte and
+ *    k_out / v_out on 2-byte boundaries.  Misaligned pointers return HS2_ERR_INVALID_ARG.
  *  - Layouts are dense and row-major in the order the dimensions are listed.
  *    q: [B, Tq, H, d]; k, v: [B, Nmax, d] (one KV head); k_scale, v_scale: [B, Nmax] fp32;
  *    q_pos: [B, Tq] int32 absolute positions; kv_len: [B] int32 valid cache rows;
@@ -80,7 +83,9 @@ typedef enum {
  * KV Bridging for one target layer (lynxflow "Two-Level KV Sharing": each target layer keeps its
  * own K/V projections; ainews mechanism paragraph).
  *   K[t, c] = bf16_rne( sum_i hidden[t, i] * w_k[i, c] ),  V likewise with w_v,
- * products and sums in fp32 (MFMA), one rounding to bf16 (nearest, ties to even) at the end.
+ * products and sums in fp32, one rounding to bf16 (nearest, ties to even) at the end.  Spans of
+ * up to 64 rows (D <= 4096) run a vector-matrix kernel that reads the weights once per four rows;
+ * longer spans run MFMA tiles of 256 rows.
  *   hidden : bf16 [T, D] row-major            w_k, w_v : bf16 [D, d] row-major
  *   k_out, v_out : bf16, row t at element offset t * out_row_stride (out_row_stride >= d), so
  *                  the rows can be written straight into a larger cache.

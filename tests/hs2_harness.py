@@ -151,7 +151,7 @@ def check_indices(idx_gpu: np.ndarray, idx_o: np.ndarray, score_o: np.ndarray, t
     return {"mismatch": int(diff.size // 2), "n": n}
 
 
-def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0):
+def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0, max_frac=1e-3):
     """GPU bridge output vs the oracle's: the bit patterns may differ only where fp32 summation
     can move the sum across a bf16 rounding boundary.  Bound per element (sampled rows):
     |gpu - exact| <= D * 2^-24 * sum_i |h_i w_i| + one bf16 ulp of the exact value."""
@@ -159,7 +159,8 @@ def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0):
     D = hidden.shape[1]
     frac_k, frac_v = float(np.mean(kb != ko)), float(np.mean(vb != vo))
     _say(f"[parity] bridge mismatch fraction K {frac_k:.2e} V {frac_v:.2e}")
-    assert frac_k < 1e-3 and frac_v < 1e-3
+    if max_frac is not None:      # a rate: meaningful over many elements only
+        assert frac_k < max_frac and frac_v < max_frac
     rows = np.random.default_rng(seed).choice(hidden.shape[0], size=min(sample, hidden.shape[0]), replace=False)
     h = oracle.decode(hidden[rows], "bf16")
     for w_bits, got in ((wk, kb), (wv, vb)):

@@ -57,6 +57,12 @@ def _fas(**kw):
     (dict(wsb=1024), hs2.HS2_ERR_WORKSPACE),
     (dict(B=-1), hs2.HS2_ERR_INVALID_ARG),
     (dict(N=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), hs2.HS2_ERR_INVALID_ARG),     # misaligned pointers
+    (dict(k=FAKE + 4), hs2.HS2_ERR_INVALID_ARG),
+    (dict(o=FAKE + 4), hs2.HS2_ERR_INVALID_ARG),
+    (dict(idx=FAKE + 2), hs2.HS2_ERR_INVALID_ARG),
+    (dict(kl=FAKE + 1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(ws=FAKE + 8), hs2.HS2_ERR_INVALID_ARG),
 ])
 def test_full_attn_select_rejects(kw, status):
     assert _fas(**kw) == status
@@ -123,6 +129,8 @@ def _spl(L=3, qarr=True, oarr=True, **kw):
     (dict(S=0), hs2.HS2_ERR_INVALID_ARG),
     (dict(d=32), hs2.HS2_ERR_UNSUPPORTED),
     (dict(B=0), hs2.HS2_OK),                          # empty batch: nothing launched
+    (dict(v=FAKE + 8), hs2.HS2_ERR_INVALID_ARG),      # misaligned pointers
+    (dict(idx=FAKE + 2), hs2.HS2_ERR_INVALID_ARG),
 ])
 def test_sparse_layers_rejects(kw, status):
     assert _spl(**kw) == status
@@ -142,6 +150,9 @@ def test_sparse_layers_workspace_size():
     ((FAKE, 10, 128, FAKE, FAKE, 128, FAKE, FAKE, 64, None), hs2.HS2_ERR_INVALID_ARG),    # stride < d
     ((None, 10, 128, FAKE, FAKE, 128, FAKE, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),
     ((None, 0, 128, None, None, 128, None, None, 128, None), hs2.HS2_OK),                 # T == 0
+    ((FAKE + 8, 10, 128, FAKE, FAKE, 128, FAKE, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),  # hidden alignment
+    ((FAKE, 10, 128, FAKE, FAKE + 2, 128, FAKE, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),  # w_v alignment
+    ((FAKE, 10, 128, FAKE, FAKE, 128, FAKE + 1, FAKE, 128, None), hs2.HS2_ERR_INVALID_ARG),  # k_out alignment
 ])
 def test_bridge_rejects(args, status):
     assert hs2.lib().hs2_kv_bridge(*args) == status

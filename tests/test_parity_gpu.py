@@ -202,6 +202,45 @@ def test_bridge_small_exact():
     assert np.array_equal(bits_from_dev(k), ko) and np.array_equal(bits_from_dev(v), vo)
 
 
+@pytest.mark.parametrize("T,D,d", [(1, 256, 128), (2, 256, 64), (3, 512, 128), (4, 256, 128), (5, 256, 64),
+                                   (8, 2048, 128), (33, 256, 128), (64, 4096, 128), (65, 256, 128),
+                                   (1, 4096, 64), (1, 4160, 128)])
+def test_bridge_few_rows_exact(T, D, d):
+    """Spans of a few rows (a decoded token's) on the vector-matrix kernel, and the sizes around its
+    limits (T = 65 and D = 4160 take the MFMA tiles): integer operands, so bit-exact."""
+    import token_level_sparse_mqa_amd as hs2
+    import oracle
+    from workloads.gen import f32_to_bf16_bits
+    rng = np.random.default_rng(T * 7919 + D + d)
+    hb = f32_to_bf16_bits(rng.integers(-3, 4, size=(T, D)).astype(np.float32))
+    wkb = f32_to_bf16_bits(rng.integers(-3, 4, size=(D, d)).astype(np.float32))
+    wvb = f32_to_bf16_bits(rng.integers(-3, 4, size=(D, d)).astype(np.float32))
+    # rows written into the middle of a larger cache (row stride 2d), the rest left untouched
+    cache = torch.full((T + 3, 2 * d), -5.0, dtype=torch.bfloat16, device="cuda")
+    hs2.hs2_kv_bridge(to_dev(hb, "bf16"), to_dev(wkb, "bf16"), to_dev(wvb, "bf16"),
+                      k_out=cache[2:2 + T, :d], v_out=cache[2:2 + T, d:], out_row_stride=2 * d)
+    c = bits_from_dev(cache)
+    ko, vo = oracle.kv_bridge(hb, wkb, wvb)
+    assert np.array_equal(c[2:2 + T, :d], ko) and np.array_equal(c[2:2 + T, d:], vo)
+    assert np.all(oracle.decode(c[:2], "bf16") == -5.0) and np.all(oracle.decode(c[2 + T:], "bf16") == -5.0)
+
+
+def test_bridge_one_row_random():
+    """One decoded token at the workload's width: random operands within the fp32 summation bound."""
+    import token_level_sparse_mqa_amd as hs2
+    import oracle
+    from workloads.gen import f32_to_bf16_bits
+    rng = np.random.default_rng(8)
+    for T in (1, 7):
+        D, d = 2048, 128
+        hb = f32_to_bf16_bits(rng.standard_normal((T, D)).astype(np.float32))
+        wkb = f32_to_bf16_bits((rng.standard_normal((D, d)) * 0.02).astype(np.float32))
+        wvb = f32_to_bf16_bits((rng.standard_normal((D, d)) * 0.02).astype(np.float32))
+        k, v = hs2.hs2_kv_bridge(to_dev(hb, "bf16"), to_dev(wkb, "bf16"), to_dev(wvb, "bf16"))
+        ko, vo = oracle.kv_bridge(hb, wkb, wvb)
+        check_bridge(hb, wkb, wvb, bits_from_dev(k), bits_from_dev(v), ko, vo, max_frac=None)
+
+
 def test_bridge_strided_rows():
     import token_level_sparse_mqa_amd as hs2
     import oracle

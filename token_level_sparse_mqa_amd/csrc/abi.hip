@@ -78,10 +78,11 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
         p.score_nsplit = p.nsplit;
         p.score_chunk = p.chunk;
     } else {
-        const int64_t min_chunk = kv_dtype == HS2_FP8_E4M3 ? 2048 : 1024;
+        const int64_t min_chunk = kv_dtype == HS2_FP8_E4M3 ? 2048 : 512;
         // attention: about four workgroups per CU over the pass; score pass: about two (one
         // wave of workgroups, so no workgroup's start-up latency falls into the stream).
-        // Both were chosen by measurement on the decode workloads.
+        // Both were chosen by measurement on the decode workloads.  The minimum chunk only binds
+        // for a few rows (one sequence at 128K keys: 257 workgroups instead of 129).
         split_range(p.R, Nmax, 1024, min_chunk, 128, &p.nsplit, &p.chunk);
         split_range(p.R, Nmax, 512, min_chunk, 128, &p.score_nsplit, &p.score_chunk);
     }
@@ -114,6 +115,9 @@ size_t sparse_ws_bytes(int64_t R, int H, int d, int S, int q_dtype) {
     return ns > 1 ? (size_t)R * ns * H * (d + 2) * 4 : 0;
 }
 
+// every kernel reads q/k/v rows, hidden states and weights in 16-byte vectors
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
 hs2_status check_common(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
                         const float* k_scale, const float* v_scale, int B, int Tq, int H, int d,
                         int64_t Nmax, float sm_scale, const float* o) {
@@ -131,6 +135,9 @@ hs2_status check_common(const void* q, int q_dtype, const void* k, const void* v
         return fail(HS2_ERR_INVALID_ARG, "k_scale/v_scale must be NULL unless the KV dtype is FP8");
     }
     if ((int64_t)B * Tq > 0 && (!q || !k || !v || !o)) return fail(HS2_ERR_INVALID_ARG, "null q/k/v/o pointer");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(HS2_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4)) return fail(HS2_ERR_INVALID_ARG, "k_scale/v_scale must be 4-byte aligned");
     return HS2_OK;
 }
 
@@ -221,9 +228,12 @@ hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D, const void* w
     if (out_row_stride < d) return fail(HS2_ERR_INVALID_ARG, "out_row_stride %lld < d", (long long)out_row_stride);
     if (T == 0) return HS2_OK;
     if (!hidden || !w_k || !w_v || !k_out || !v_out) return fail(HS2_ERR_INVALID_ARG, "null pointer");
+    if (!aligned(hidden, 16) || !aligned(w_k, 16) || !aligned(w_v, 16) || !aligned(k_out, 2) || !aligned(v_out, 2))
+        return fail(HS2_ERR_INVALID_ARG, "hidden/w_k/w_v must be 16-byte and k_out/v_out 2-byte aligned");
     BridgeArgs a{(const uint16_t*)hidden, T, D, (const uint16_t*)w_k, (const uint16_t*)w_v, d,
                  (uint16_t*)k_out, (uint16_t*)v_out, out_row_stride};
-    hipError_t e = launch_bridge_mfma(a, stream);
+    // a few rows (a decoded token's) take the vector-matrix kernel, longer spans the MFMA tiles
+    hipError_t e = bridge_rows_fits(a) ? launch_bridge_rows(a, stream) : launch_bridge_mfma(a, stream);
     if (e != hipSuccess) return hip_fail(e, "kv_bridge launch");
     return HS2_OK;
 }
@@ -248,6 +258,8 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
     if ((int64_t)B * Tq == 0) return HS2_OK;
     if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
+    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(scores_dbg, 4) || !aligned(workspace, 16))
+        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx/scores_dbg must be 4-byte and the workspace 16-byte aligned");
     const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
     if (!workspace || workspace_bytes < p.total)
         return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
@@ -338,6 +350,8 @@ hs2_status hs2_sparse_attn_layers(const void* const* q, int32_t L, hs2_dtype q_d
     if (S < 1 || S > 8192) return fail(HS2_ERR_INVALID_ARG, "S=%d outside [1, 8192]", S);
     if ((int64_t)B * Tq == 0) return HS2_OK;
     if (!idx) return fail(HS2_ERR_INVALID_ARG, "null idx pointer");
+    if (!aligned(idx, 4) || !aligned(kv_len, 4) || !aligned(workspace, 16))
+        return fail(HS2_ERR_INVALID_ARG, "idx/kv_len must be 4-byte and the workspace 16-byte aligned");
     const int64_t R = (int64_t)B * Tq;
     const size_t need = sparse_ws_bytes(R, H, d, S, q_dtype);        // per layer
     const bool split = workspace && need > 0 && workspace_bytes >= need * (size_t)L;

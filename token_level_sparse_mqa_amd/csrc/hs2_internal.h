@@ -85,6 +85,8 @@ hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t 
 hipError_t launch_score_generic(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s);
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s);
+bool bridge_rows_fits(const BridgeArgs& a);
+hipError_t launch_bridge_rows(const BridgeArgs& a, hipStream_t s);
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_rows_mfma(const ScoreArgs& a, hipStream_t s);
