@@ -30,6 +30,10 @@ What the hot path computes, written as plain definitions (numpy, float64):
   agentik-os section 2; ainews mechanism paragraph).
 * FP8 caches (ainews experimental-setup paragraph): OCP E4M3FN codes times a per-row
   fp32 scale.
+* Block-level selection, the first-generation scheme the pages compare against (kucoin
+  news flash; lynxflow "Token-Level Sparse Selection"): candidates in groups of 64, a
+  group kept whole when any member is important.  Read here with the same score and the
+  same budget: block score = max of its members' scores, the 1024/64 = 16 best blocks.
 
 Every function is pinned by tests under tests/test_oracle_*.py against closed forms,
 library routines, brute force and invariants.
@@ -183,6 +187,49 @@ def full_attn_select(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndar
         out[(b, i)] = full_attn_select_row(q[b, i], k[b], v[b], int(q_pos[b, i]), sm,
                                            k_global, window)
     return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Block-level selection (the first-generation variant the token-level one replaces)
+# ----------------------------------------------------------------------------------------------
+BLOCK = 64
+
+
+def block_scores(score: np.ndarray, block: int) -> np.ndarray:
+    """Candidates grouped in consecutive blocks of `block` positions (the last block may be
+    shorter); a block's score is the largest score of its members, so a block ranks as high as
+    its most important token (kucoin news flash: groups of 64 kept whole when any member is
+    important).  score [C] -> [ceil(C / block)]."""
+    C = score.shape[0]
+    nb = -(-C // block)
+    return np.array([score[b * block: min(C, (b + 1) * block)].max() for b in range(nb)], dtype=np.float64)
+
+
+def select_blocks(score: np.ndarray, k_blocks: int, block: int) -> np.ndarray:
+    """The min(k_blocks, #blocks) best blocks by (block score descending, block id ascending),
+    as ascending block ids: the token rule applied to blocks, with the same budget of
+    k_blocks * block positions."""
+    return select_global(block_scores(score, block), k_blocks)
+
+
+def expand_blocks(blocks: np.ndarray, C: int, block: int) -> np.ndarray:
+    """Every candidate position of the chosen blocks, ascending (a block past C is cut at C)."""
+    parts = [np.arange(b * block, min(C, (b + 1) * block)) for b in np.asarray(blocks, dtype=np.int64)]
+    return np.concatenate(parts) if parts else np.zeros(0, dtype=np.int64)
+
+
+def full_attn_select_blocks_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, t: int, sm: float,
+                                k_blocks: int = K_GLOBAL // BLOCK, block: int = BLOCK,
+                                window: int = WINDOW):
+    """One query token with block-level selection: (o [H,d], block ids [k_blocks] ascending with
+    -1 padding, idx [k_blocks * block + W] in the token layout, score [C])."""
+    o, p = dense_attention(q, k, v, t, sm)
+    score = selection_scores(p, t, window)
+    blocks = select_blocks(score, k_blocks, block)
+    bid = np.full(k_blocks, -1, dtype=np.int32)
+    bid[: blocks.shape[0]] = blocks
+    idx = assemble_indices(expand_blocks(blocks, score.shape[0], block), t, k_blocks * block, window)
+    return o, bid, idx, score
 
 
 # ----------------------------------------------------------------------------------------------

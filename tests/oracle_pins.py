@@ -264,7 +264,70 @@ def check_bridge(O):
     assert np.array_equal(O.bf16_bits_to_f64(kk)[0], np.array([1.0, 1.0 + 2.0 ** -6]))
 
 
+def _block_beats(s, a, b, block):
+    """Block a outranks block b: some member of a scores above every member of b, or neither
+    block has such a member (equal maxima) and a comes first."""
+    A = s[a * block: (a + 1) * block]
+    Bm = s[b * block: (b + 1) * block]
+    a_over = any(all(x > y for y in Bm) for x in A)
+    b_over = any(all(y > x for x in A) for y in Bm)
+    return a_over or (not b_over and a < b)
+
+
+def check_block_selection(O):
+    """Block-level selection from its definition: a block is kept iff fewer than k_b blocks
+    outrank it (brute force, tiny inputs with many ties); block = 1 is token-level selection;
+    a block with one important member is kept whole; the maximum, not the sum, ranks blocks;
+    a short last block is cut at the candidate count."""
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        block = int(rng.choice([1, 2, 3, 4]))
+        C = int(rng.integers(1, 14))
+        s = rng.integers(0, 4, size=C).astype(np.float64)
+        nb = -(-C // block)
+        for kb in range(0, nb + 2):
+            exp = [b for b in range(nb) if sum(1 for a in range(nb) if a != b and _block_beats(s, a, b, block)) < kb]
+            got = O.select_blocks(s, kb, block)
+            assert got.tolist() == exp, (s.tolist(), block, kb, got, exp)
+            toks = O.expand_blocks(got, C, block)
+            assert toks.tolist() == [j for b in exp for j in range(b * block, min(C, (b + 1) * block))]
+        if block == 1:
+            for kb in range(0, C + 2):
+                assert np.array_equal(O.select_blocks(s, kb, 1), O.select_global(s, kb))
+    # one important member keeps its whole group of 64
+    s = np.full(64 * 40, 1e-4)
+    s[64 * 17 + 5] = 0.9
+    s[64 * 3: 64 * 4] = 0.5                    # a whole group of medium members
+    assert O.select_blocks(s, 1, 64).tolist() == [17]      # the maximum ranks, not the sum (32.0)
+    assert O.expand_blocks(O.select_blocks(s, 2, 64), s.shape[0], 64).tolist() == \
+        list(range(64 * 3, 64 * 4)) + list(range(64 * 17, 64 * 18))
+    # a short last block: C = 64 * 5 + 7, its best member is the last candidate
+    s = np.zeros(64 * 5 + 7)
+    s[-1] = 1.0
+    assert O.select_blocks(s, 1, 64).tolist() == [5]
+    assert O.expand_blocks([5], s.shape[0], 64).tolist() == list(range(320, 327))
+
+
+def check_block_rows(O, k_b=16, block=64, W=128):
+    """Whole rows on identical keys (all scores equal): the lowest blocks, the token layout of
+    the indices (global budget k_b * block, then the window), for positions around the edges."""
+    H, d = 2, 4
+    for t in (0, 127, 128, 191, 192, 300, 1151, 1152, 1200, 1500):
+        N = t + 1
+        k = np.ones((N, d))
+        v = np.arange(N * d, dtype=np.float64).reshape(N, d)
+        q = np.ones((H, d))
+        o, bid, idx, score = O.full_attn_select_blocks_row(q, k, v, t, 0.5, k_b, block, W)
+        C = max(0, t - W + 1)
+        nb = -(-C // block)
+        assert bid.tolist() == list(range(min(k_b, nb))) + [-1] * (k_b - min(k_b, nb))
+        g = list(range(min(C, k_b * block)))
+        win = list(range(max(0, t - W + 1), t + 1))
+        assert idx.tolist() == g + [-1] * (k_b * block - len(g)) + win + [-1] * (W - len(win))
+        assert np.allclose(o, v.mean(axis=0)[None, :], rtol=0, atol=1e-12)
+
+
 ALL_CHECKS = [check_dense_vs_sdpa, check_identical_keys, check_score_mass, check_onehot_keys,
               check_selection_bruteforce, check_selection_exhaustive, check_window_enumeration,
               check_sparse_identity, check_sparse_order_invariance, check_needles, check_bf16,
-              check_e4m3fn, check_bridge]
+              check_e4m3fn, check_bridge, check_block_selection, check_block_rows]

@@ -57,6 +57,12 @@ MUTATIONS = [
     ("bridge truncates instead of RNE", "np.round(ax / spacing)", "np.floor(ax / spacing)"),
     ("bf16 decode drops the low byte", "u = np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)",
      "u = (np.asarray(u16, dtype=np.uint16).astype(np.uint32) & np.uint32(0xFF00)) << np.uint32(16)"),
+    ("block score is the sum of its members", "min(C, (b + 1) * block)].max() for b in range(nb)",
+     "min(C, (b + 1) * block)].sum() for b in range(nb)"),
+    ("short last block runs past the candidates", "np.arange(b * block, min(C, (b + 1) * block))",
+     "np.arange(b * block, (b + 1) * block)"),
+    ("blocks shifted by one position", "score[b * block: min(C, (b + 1) * block)]",
+     "score[b * block + 1: min(C, (b + 1) * block + 1)]"),
     ("sparse softmax without max shift cancels nothing but wrong normaliser",
      "p = e / e.sum(axis=1, keepdims=True)\n    return p @ v[sel]",
      "p = e / e.sum()\n    return p @ v[sel]"),
