@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "query tokens/s for select+sparse attn at 128K & 1M ctx; % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+BLOCK = 64                      # block-level selection: positions per block
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -131,7 +132,7 @@ def stored_traffic(workload, kernel):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def run_gpu(cfg, steps, warmup, profile=True):
+def run_gpu(cfg, steps, warmup, profile=True, select="token"):
     import torch
 
     import token_level_sparse_mqa_amd as hs2
@@ -144,8 +145,16 @@ def run_gpu(cfg, steps, warmup, profile=True):
     sm = 1.0 / math.sqrt(cfg.d)
     R = cfg.B * cfg.Tq
     kvd = hs2.dtype_code(t["k"])
-    ws = torch.empty((hs2.hs2_full_attn_select_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global,
-                                                               cfg.window, kvd),), dtype=torch.uint8, device=dev)
+    blocks = select == "blocks"
+    kb = cfg.k_global // BLOCK
+    if blocks:
+        nws = hs2.hs2_full_attn_select_blocks_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, kb, BLOCK,
+                                                             cfg.window, kvd)
+    else:
+        nws = hs2.hs2_full_attn_select_workspace_size(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global, cfg.window,
+                                                      kvd)
+    ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
+    bidx = torch.empty((cfg.B, cfg.Tq, kb), dtype=torch.int32, device=dev)
     sws = hs2.sparse_attn_layers_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, cfg.n_sparse, dev)
     o = torch.empty((cfg.B, cfg.Tq, cfg.H, cfg.d), dtype=torch.float32, device=dev)
     idx = torch.empty((cfg.B, cfg.Tq, cfg.S), dtype=torch.int32, device=dev)
@@ -154,9 +163,14 @@ def run_gpu(cfg, steps, warmup, profile=True):
     def step():
         if cfg.bridge_D:
             hs2.hs2_kv_bridge(t["hidden"], t["wk"], t["wv"], k_out=t["k"][0], v_out=t["v"][0])
-        hs2.hs2_full_attn_select(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
-                                 v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
-                                 o=o, idx=idx, workspace=ws)
+        if blocks:
+            hs2.hs2_full_attn_select_blocks(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
+                                            v_scale=t["v_scale"], k_blocks=kb, block=BLOCK, window=cfg.window,
+                                            sm_scale=sm, o=o, block_idx=bidx, idx=idx, workspace=ws)
+        else:
+            hs2.hs2_full_attn_select(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
+                                     v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
+                                     o=o, idx=idx, workspace=ws)
         # the sparse layers share the K/V cache and the indices: one call (one launch per kernel)
         hs2.hs2_sparse_attn_layers(t["qs"], t["k"], t["v"], idx, kv_len=t["kv_len"], k_scale=t["k_scale"],
                                    v_scale=t["v_scale"], sm_scale=sm, os=o_sp, workspace=sws)
@@ -405,7 +419,7 @@ def gather_cold_sweep(reps=5):
                      "1 GiB bf16 K+V cache (not the timed step)", "points": out}
 
 
-def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0):
+def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0, select="token"):
     """The float64 oracle, as it stands, on a bounded sample of the same workload: whole query
     rows, each with the full layer, the selection and every sparse layer, including decoding
     the cache bytes.  Small workloads are repeated until min_s of work; large ones stop after
@@ -435,7 +449,11 @@ def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0):
             k, v = decoded[b]
             q = oracle.decode(wl.q_full[b, i], cfg.q_dtype)
             t = int(wl.q_pos[b, i])
-            _, idx, _ = oracle.full_attn_select_row(q, k, v, t, sm, cfg.k_global, cfg.window)
+            if select == "blocks":
+                _, _, idx, _ = oracle.full_attn_select_blocks_row(q, k, v, t, sm, cfg.k_global // BLOCK, BLOCK,
+                                                                  cfg.window)
+            else:
+                _, idx, _ = oracle.full_attn_select_row(q, k, v, t, sm, cfg.k_global, cfg.window)
             for l in range(cfg.n_sparse):
                 oracle.sparse_attention_row(oracle.decode(wl.q_sparse[l][b, i], cfg.q_dtype), k, v, idx, sm)
             done += 1
@@ -446,7 +464,7 @@ def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0):
             break
     return {"value": done / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} query rows of {cfg.name} ({passes} pass(es) over its {len(rows)} rows; each "
-                      f"row: full layer + selection + {cfg.n_sparse} sparse layers, incl. decoding the "
+                      f"row: full layer + {'block' if select == 'blocks' else 'token'}-level selection + {cfg.n_sparse} sparse layers, incl. decoding the "
                       f"cache), {el:.1f} s"}
 
 
@@ -456,6 +474,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode128k")
+    ap.add_argument("--select", choices=("token", "blocks"), default="token",
+                    help="token-level selection (the method) or the 64-token block-level variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-gather-sweep", action="store_true",
@@ -483,7 +503,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
+    res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile, select=args.select)
     ms = res["ms_per_step"]
     value = res["rows"] / (ms / 1e3)
     alg = algorithmic(cfg)
@@ -515,7 +535,8 @@ def main():
         ("+fp8kv" if cfg.kv_dtype == "fp8" else ""), "data": "synthetic",
         "config": {"workload": cfg.name, "B": cfg.B, "context": cfg.N, "Tq": cfg.Tq, "H": cfg.H, "d": cfg.d,
                    "kv_dtype": cfg.kv_dtype, "k_global": cfg.k_global, "window": cfg.window,
-                   "sparse_layers": cfg.n_sparse, "bridge_D": cfg.bridge_D},
+                   "sparse_layers": cfg.n_sparse, "bridge_D": cfg.bridge_D,
+                   "selection": "token" if args.select == "token" else f"blocks of {BLOCK}"},
         "roofline": roof, "step_roofline_frac": step_frac, "kernels": kernels,
     }
     if cfg.Tq == 1 and not args.no_gather_sweep and not args.no_profile:
@@ -523,7 +544,7 @@ def main():
         out["gather_cold_sweep"] = gather_cold_sweep()
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(cfg, res["wl"])
+        out["cpu_baseline"] = cpu_baseline(cfg, res["wl"], select=args.select)
     print(json.dumps(out), flush=True)
 
 

@@ -128,6 +128,43 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Bytes of workspace hs2_full_attn_select_blocks needs for these sizes (0 on invalid sizes).
+ */
+size_t hs2_full_attn_select_blocks_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d,
+                                                  int64_t Nmax, int32_t k_blocks, int32_t block,
+                                                  int32_t window, hs2_dtype kv_dtype);
+
+/*
+ * Full-attention MQA layer with block-level selection: the first-generation scheme that the
+ * token-level selection replaces (kucoin news flash: groups of 64 tokens, a group kept whole
+ * when any member is important; lynxflow "Token-Level Sparse Selection"), on the same score and
+ * the same budget of k_blocks * block positions.
+ *   o, score(j), the candidates j = 0..C-1 (C = t-window+1, or 0) and the window: as in
+ *   hs2_full_attn_select.
+ *   Block b holds the candidates b*block .. min(C, (b+1)*block) - 1; its score is the largest
+ *   score(j) of its members.
+ *   block_idx[b,i, 0:k_blocks] = the min(k_blocks, #blocks) best blocks by (block score desc,
+ *                                block id asc), ascending, then -1 padding;
+ *   idx[b,i, 0:k_blocks*block] = every member of those blocks, ascending, then -1 padding;
+ *   idx[b,i, k_blocks*block : k_blocks*block+window] = the window, as in hs2_full_attn_select.
+ * idx has the token-level layout with k_global = k_blocks * block, so hs2_sparse_attn and
+ * hs2_sparse_attn_layers consume it unchanged (S = k_blocks * block + window).
+ * Requirements: block a power of two in [1, 64]; 1 <= k_blocks, k_blocks * block <= 4096;
+ *   ceil(Nmax / block) <= 16384 (otherwise HS2_ERR_UNSUPPORTED); 0 <= window <= 4096;
+ *   workspace_bytes >= hs2_full_attn_select_blocks_workspace_size(...); other arguments as for
+ *   hs2_full_attn_select.  block = 1 gives exactly the token-level selection.
+ */
+hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype,
+                                       const void* k, const void* v, hs2_dtype kv_dtype,
+                                       const float* k_scale, const float* v_scale,
+                                       const int32_t* q_pos, const int32_t* kv_len,
+                                       int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                       int32_t k_blocks, int32_t block, int32_t window,
+                                       float sm_scale, float* o, int32_t* block_idx, int32_t* idx,
+                                       float* scores_dbg, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * Sparse (index-reusing) attention layer (KV Reuse).
  *   o[b,i,h] = sum_{j in sel} softmax_j(sm_scale * q_h . k_j) v_j,
  *   sel = { idx[b,i,e] : 0 <= e < S, 0 <= idx[b,i,e] < min(kv_len[b], Nmax) }.

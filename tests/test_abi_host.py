@@ -107,6 +107,48 @@ def test_sparse_rejects(kw, status):
     assert _sp(**kw) == status
 
 
+def _fasb(**kw):
+    a = dict(q=FAKE, qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, qp=FAKE, kl=FAKE,
+             B=1, Tq=1, H=32, d=128, N=4096, kb=16, blk=64, W=128, sm=0.088, o=FAKE, bidx=FAKE, idx=FAKE,
+             dbg=None, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return hs2.lib().hs2_full_attn_select_blocks(a["q"], a["qd"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"],
+                                                 a["qp"], a["kl"], a["B"], a["Tq"], a["H"], a["d"], a["N"], a["kb"],
+                                                 a["blk"], a["W"], a["sm"], a["o"], a["bidx"], a["idx"], a["dbg"],
+                                                 a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(blk=3), hs2.HS2_ERR_INVALID_ARG),              # not a power of two
+    (dict(blk=128), hs2.HS2_ERR_INVALID_ARG),            # above 64
+    (dict(blk=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(kb=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(kb=65), hs2.HS2_ERR_INVALID_ARG),              # 65 * 64 > 4096
+    (dict(N=(16384 * 64) + 1), hs2.HS2_ERR_UNSUPPORTED), # more than 16384 blocks per row
+    (dict(blk=1, N=16385), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(bidx=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(bidx=FAKE + 2), hs2.HS2_ERR_INVALID_ARG),
+    (dict(W=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(d=96), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
+    (dict(wsb=4096), hs2.HS2_ERR_WORKSPACE),
+    (dict(B=0, q=None, k=None, v=None, o=None, idx=None, bidx=None, ws=None), hs2.HS2_OK),
+])
+def test_full_attn_select_blocks_rejects(kw, status):
+    assert _fasb(**kw) == status
+    if status != hs2.HS2_OK:
+        assert hs2.hs2_last_error()
+
+
+def test_blocks_workspace_size():
+    tok = hs2.hs2_full_attn_select_workspace_size(8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16)
+    blk = hs2.hs2_full_attn_select_blocks_workspace_size(8, 1, 32, 128, 131072, 16, 64, 128, hs2.HS2_BF16)
+    # the token-level plan plus the block maxima [R, Nmax / 64] fp32
+    assert blk >= tok + 8 * 2048 * 4
+    assert hs2.hs2_full_attn_select_blocks_workspace_size(8, 1, 32, 128, 131072, 16, 48, 128, hs2.HS2_BF16) == 0
+    assert hs2.hs2_full_attn_select_blocks_workspace_size(1, 1, 32, 128, 1 << 21, 16, 64, 128, hs2.HS2_BF16) == 0
+
+
 def _spl(L=3, qarr=True, oarr=True, **kw):
     a = dict(qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, idx=FAKE, S=1152,
              kl=None, B=1, Tq=1, H=32, d=128, N=4096, sm=0.088, ws=None, wsb=0, stream=None)

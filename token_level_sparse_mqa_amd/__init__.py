@@ -5,6 +5,7 @@ called through its C ABI (include/hs2.h) with ctypes.  torch provides device mem
 the current stream.  The functions carry the C names:
 
     hs2_kv_bridge, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
+    hs2_full_attn_select_blocks, hs2_full_attn_select_blocks_workspace_size,
     hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_sparse_attn_layers,
     hs2_sparse_attn_layers_workspace_size, hs2_last_error, hs2_version
 
@@ -33,6 +34,11 @@ _SIGS = {
     "hs2_full_attn_select": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                             _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
                                             _vp, _vp, _vp, _vp, _sz, _vp]),
+    "hs2_full_attn_select_blocks_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
+                                                         ctypes.c_int]),
+    "hs2_full_attn_select_blocks": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                   _i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32, _f32,
+                                                   _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "hs2_sparse_attn": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _vp,
                                        _i32, _i32, _i32, _i32, _i64, _f32, _vp, _vp, _sz, _vp]),
     "hs2_sparse_attn_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
@@ -166,6 +172,42 @@ def hs2_full_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_po
         B, Tq, H, d, Nmax, k_global, window, float(sm_scale), _ptr(o), _ptr(idx), _ptr(scores_dbg),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
     return o, idx
+
+
+def hs2_full_attn_select_blocks_workspace_size(B: int, Tq: int, H: int, d: int, Nmax: int, k_blocks: int,
+                                               block: int, window: int, kv_dtype: int) -> int:
+    return int(lib().hs2_full_attn_select_blocks_workspace_size(B, Tq, H, d, Nmax, k_blocks, block, window,
+                                                                kv_dtype))
+
+
+def hs2_full_attn_select_blocks(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+                                kv_len: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
+                                v_scale: Optional[torch.Tensor] = None, k_blocks: int = 16, block: int = 64,
+                                window: int = 128, sm_scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                                block_idx: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                                scores_dbg: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                                stream=None):
+    """Full-attention MQA layer + block-level selection.  Returns (o fp32 [B,Tq,H,d],
+    block_idx int32 [B,Tq,k_blocks], idx int32 [B,Tq,k_blocks*block+window])."""
+    B, Tq, H, d = q.shape
+    Nmax = k.shape[1]
+    kvd = dtype_code(k)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
+    if block_idx is None:
+        block_idx = torch.empty((B, Tq, k_blocks), dtype=torch.int32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Tq, k_blocks * block + window), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        n = hs2_full_attn_select_blocks_workspace_size(B, Tq, H, d, Nmax, k_blocks, block, window, kvd)
+        workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=q.device)
+    _check(lib().hs2_full_attn_select_blocks(
+        _ptr(q), dtype_code(q), _ptr(k), _ptr(v), kvd, _ptr(k_scale), _ptr(v_scale), _ptr(q_pos), _ptr(kv_len),
+        B, Tq, H, d, Nmax, k_blocks, block, window, float(sm_scale), _ptr(o), _ptr(block_idx), _ptr(idx),
+        _ptr(scores_dbg), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, block_idx, idx
 
 
 def hs2_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,

@@ -247,24 +247,14 @@ size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int
     return plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype).total;
 }
 
-hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
-                                const float* k_scale, const float* v_scale, const int32_t* q_pos,
-                                const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
-                                int32_t k_global, int32_t window, float sm_scale, float* o, int32_t* idx,
-                                float* scores_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
-    if (st != HS2_OK) return st;
-    if (k_global < 1 || k_global > 4096) return fail(HS2_ERR_INVALID_ARG, "k_global=%d outside [1, 4096]", k_global);
-    if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
-    if ((int64_t)B * Tq == 0) return HS2_OK;
-    if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
-    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(scores_dbg, 4) || !aligned(workspace, 16))
-        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx/scores_dbg must be 4-byte and the workspace 16-byte aligned");
-    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
-    if (!workspace || workspace_bytes < p.total)
-        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
+namespace {
 
-    char* ws = (char*)workspace;
+// The full layer up to the token scores: attention (o, per-head log-sum-exp) and the score pass.
+// Shared by the token-level and the block-level selection.
+hs2_status full_layer(const SelectPlan& p, const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                      const float* k_scale, const float* v_scale, const int32_t* q_pos, const int32_t* kv_len,
+                      int B, int Tq, int H, int d, int64_t Nmax, int window, float sm_scale, float* o, char* ws,
+                      hipStream_t stream) {
     float* lse = (float*)(ws + p.off_lse);
     float* scores = (float*)(ws + p.off_scores);
     uint32_t* rowhist = (uint32_t*)(ws + p.off_hist);
@@ -302,14 +292,102 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     e = p.path == PATH_GENERIC ? launch_score_generic(sa, stream)
         : p.path == PATH_MFMA_PREFILL ? launch_score_prefill(sa, stream) : launch_score_rows_mfma(sa, stream);
     if (e != hipSuccess) return hip_fail(e, "score launch");
+    return HS2_OK;
+}
 
+SelectArgs select_args(const SelectPlan& p, char* ws, const int32_t* q_pos, const int32_t* kv_len, int Tq,
+                       int64_t Nmax, int k_global, int window, int32_t* idx, float* scores_dbg) {
     SelectArgs se{};
     se.q_pos = q_pos; se.kv_len = kv_len; se.R = (int)p.R; se.Tq = Tq; se.Nmax = Nmax;
-    se.k_global = k_global; se.window = window; se.scores = scores; se.cstride = Nmax;
-    se.rowhist = rowhist; se.counters = counters; se.sure = (int32_t*)(ws + p.off_sure);
-    se.cand = (uint2*)(ws + p.off_cand); se.nseg = p.nseg; se.idx = idx; se.scores_dbg = scores_dbg;
-    e = launch_select(se, /*hist_done=*/true, stream);
+    se.k_global = k_global; se.window = window; se.scores = (float*)(ws + p.off_scores); se.cstride = Nmax;
+    se.rowhist = (uint32_t*)(ws + p.off_hist); se.counters = (uint32_t*)(ws + p.off_cnt);
+    se.sure = (int32_t*)(ws + p.off_sure); se.cand = (uint2*)(ws + p.off_cand); se.nseg = p.nseg;
+    se.idx = idx; se.scores_dbg = scores_dbg;
+    return se;
+}
+
+// the block maxima follow the token-level plan's workspace
+size_t block_ws_extra(int64_t R, int64_t Nmax, int block) {
+    return align_up((size_t)R * (size_t)((Nmax + block - 1) / block) * 4);
+}
+
+}  // namespace
+
+hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
+                                const float* k_scale, const float* v_scale, const int32_t* q_pos,
+                                const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                int32_t k_global, int32_t window, float sm_scale, float* o, int32_t* idx,
+                                float* scores_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st != HS2_OK) return st;
+    if (k_global < 1 || k_global > 4096) return fail(HS2_ERR_INVALID_ARG, "k_global=%d outside [1, 4096]", k_global);
+    if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
+    if ((int64_t)B * Tq == 0) return HS2_OK;
+    if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
+    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(scores_dbg, 4) || !aligned(workspace, 16))
+        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx/scores_dbg must be 4-byte and the workspace 16-byte aligned");
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
+    if (!workspace || workspace_bytes < p.total)
+        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
+    char* ws = (char*)workspace;
+    st = full_layer(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax, window,
+                    sm_scale, o, ws, stream);
+    if (st != HS2_OK) return st;
+    const SelectArgs se = select_args(p, ws, q_pos, kv_len, Tq, Nmax, k_global, window, idx, scores_dbg);
+    hipError_t e = launch_select(se, /*hist_done=*/true, stream);
     if (e != hipSuccess) return hip_fail(e, "select launch");
+    return HS2_OK;
+}
+
+size_t hs2_full_attn_select_blocks_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                                  int32_t k_blocks, int32_t block, int32_t window,
+                                                  hs2_dtype kv_dtype) {
+    (void)window;
+    if (block < 1 || block > 64 || (block & (block - 1)) || k_blocks < 1 || (int64_t)k_blocks * block > 4096)
+        return 0;
+    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1) return 0;
+    if ((Nmax + block - 1) / block > kBlkMaxCand) return 0;
+    if ((int64_t)B * Tq == 0) return kAlign;
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_blocks * block, kv_dtype);
+    return p.total + block_ws_extra(p.R, Nmax, block);
+}
+
+hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype, const void* k, const void* v,
+                                       hs2_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                       const int32_t* q_pos, const int32_t* kv_len, int32_t B, int32_t Tq,
+                                       int32_t H, int32_t d, int64_t Nmax, int32_t k_blocks, int32_t block,
+                                       int32_t window, float sm_scale, float* o, int32_t* block_idx, int32_t* idx,
+                                       float* scores_dbg, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st != HS2_OK) return st;
+    if (block < 1 || block > 64 || (block & (block - 1)))
+        return fail(HS2_ERR_INVALID_ARG, "block=%d must be a power of two in [1, 64]", block);
+    if (k_blocks < 1 || (int64_t)k_blocks * block > 4096)
+        return fail(HS2_ERR_INVALID_ARG, "k_blocks=%d: need 1 <= k_blocks and k_blocks * block <= 4096", k_blocks);
+    if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
+    if ((Nmax + block - 1) / block > kBlkMaxCand)
+        return fail(HS2_ERR_UNSUPPORTED, "Nmax=%lld: at most %d blocks per row", (long long)Nmax, kBlkMaxCand);
+    if ((int64_t)B * Tq == 0) return HS2_OK;
+    if (!q_pos || !kv_len || !idx || !block_idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx/block_idx pointer");
+    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(block_idx, 4) ||
+        !aligned(scores_dbg, 4) || !aligned(workspace, 16))
+        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx/block_idx/scores_dbg must be 4-byte and the workspace 16-byte aligned");
+    const int K = k_blocks * block;
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, K, kv_dtype);
+    const size_t need = p.total + block_ws_extra(p.R, Nmax, block);
+    if (!workspace || workspace_bytes < need)
+        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+    char* ws = (char*)workspace;
+    st = full_layer(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax, window,
+                    sm_scale, o, ws, stream);
+    if (st != HS2_OK) return st;
+    SelectArgs se = select_args(p, ws, q_pos, kv_len, Tq, Nmax, K, window, idx, scores_dbg);
+    se.block = block; se.k_blocks = k_blocks;
+    se.bscore = (float*)(ws + p.total); se.bstride = (Nmax + block - 1) / block;
+    se.block_idx = block_idx;
+    hipError_t e = launch_select_blocks(se, stream);
+    if (e != hipSuccess) return hip_fail(e, "block select launch");
     return HS2_OK;
 }
 

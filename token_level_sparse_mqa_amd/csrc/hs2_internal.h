@@ -16,6 +16,7 @@ constexpr int kSelCap = 4096;
 constexpr int kHistBins = 2048;
 // Row segment handled by one select workgroup.
 constexpr int kSelSeg = 4096;
+constexpr int kBlkMaxCand = 16384;   // candidate blocks per row of the block-level selection
 
 // One attention problem: R = B*Tq query rows, each over a key set given either as the causal
 // range [0, t] (list == nullptr) or as an index list idx[r, 0:S].
@@ -71,6 +72,10 @@ struct SelectArgs {
     int nseg;
     int32_t* idx;                        // [R, k_global + window]
     float* scores_dbg;                   // [R, Nmax] or nullptr
+    // block-level selection (k_global = k_blocks * block)
+    int block, k_blocks;
+    float* bscore; int64_t bstride;      // [R, bstride] block maxima
+    int32_t* block_idx;                  // [R, k_blocks]
 };
 
 struct BridgeArgs {
@@ -84,6 +89,7 @@ hipError_t launch_attn_generic(const AttnArgs& a, const char* name, hipStream_t 
 hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_generic(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s);
+hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t s);
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s);
 bool bridge_rows_fits(const BridgeArgs& a);
 hipError_t launch_bridge_rows(const BridgeArgs& a, hipStream_t s);
