@@ -30,6 +30,9 @@ What the hot path computes, written as plain definitions (numpy, float64):
   agentik-os section 2; ainews mechanism paragraph).
 * FP8 caches (ainews experimental-setup paragraph): OCP E4M3FN codes times a per-row
   fp32 scale.
+* Multi-target FP8 bridge: every cross-decoder full layer projects the same hidden states
+  with its own Wk, Wv (lynxflow "Two-Level KV Sharing") into an FP8 cache (ainews
+  experimental-setup paragraph): per row, scale = amax/448 in fp32, codes = E4M3FN of x/scale.
 * Block-level selection, the first-generation scheme the pages compare against (kucoin
   news flash; lynxflow "Token-Level Sparse Selection"): candidates in groups of 64, a
   group kept whole when any member is important.  Read here with the same score and the
@@ -123,6 +126,56 @@ def kv_bridge(hidden_bf16: np.ndarray, wk_bf16: np.ndarray, wv_bf16: np.ndarray,
         k[r0:r0 + row_block] = f64_to_bf16_bits_rne(h @ wk)
         v[r0:r0 + row_block] = f64_to_bf16_bits_rne(h @ wv)
     return k, v
+
+
+FP8_MAX = 448.0
+
+
+def e4m3fn_encode_rne(y: np.ndarray) -> np.ndarray:
+    """Values -> OCP E4M3FN codes: the nearest finite code (ties to the even code, i.e. even
+    mantissa), saturating at +-448; the sign bit follows the value's sign (-0 -> 0x80).  Written
+    as a search over the 127 non-negative finite code values."""
+    table = e4m3fn_bits_to_f64(np.arange(0x7F, dtype=np.uint8))        # ascending: 0 .. 448
+    y = np.asarray(y, dtype=np.float64)
+    a = np.minimum(np.abs(y), FP8_MAX)
+    hi = np.clip(np.searchsorted(table, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(take_hi, hi, lo).astype(np.uint8)
+    return code | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))
+
+
+def kv_bridge_fp8(hidden_bf16: np.ndarray, wk_t_bf16, wv_t_bf16, row_block: int = 8192):
+    """Multi-target KV bridge into FP8 caches.  Every target layer has its own projections
+    (lynxflow "Two-Level KV Sharing"); here all targets project the same hidden states.
+    hidden [T, D] bf16 bits; wk_t_bf16 / wv_t_bf16: one [d, D] bf16 matrix per target (a linear
+    layer's weight: output rows).  Per target and row: x = H.W^T with float64 products and sums,
+    taken to fp32 (the precision the quantisation decides in); scale = fp32(amax|x| / 448) (1 when
+    the row is all zero); codes = E4M3FN(fp32(x / scale)).
+    Returns a list of (k_codes [T, d] u8, k_scale [T] f32, v_codes, v_scale), one per target."""
+    T = hidden_bf16.shape[0]
+    out = []
+    for wk_b, wv_b in zip(wk_t_bf16, wv_t_bf16):
+        res = []
+        for w_b in (wk_b, wv_b):
+            w = bf16_bits_to_f64(w_b)
+            d = w.shape[0]
+            codes = np.empty((T, d), dtype=np.uint8)
+            scale = np.empty((T,), dtype=np.float32)
+            for r0 in range(0, T, row_block):
+                h = bf16_bits_to_f64(hidden_bf16[r0:r0 + row_block])
+                x = (h @ w.T).astype(np.float32)
+                amax = np.abs(x).max(axis=1)
+                sc = (amax / np.float32(FP8_MAX)).astype(np.float32)
+                sc = np.where(amax > 0, sc, np.float32(1.0)).astype(np.float32)
+                y = (x / sc[:, None]).astype(np.float32)
+                codes[r0:r0 + row_block] = e4m3fn_encode_rne(y.astype(np.float64))
+                scale[r0:r0 + row_block] = sc
+            res += [codes, scale]
+        out.append(tuple(res))
+    return out
 
 
 # ----------------------------------------------------------------------------------------------

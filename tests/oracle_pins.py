@@ -327,7 +327,67 @@ def check_block_rows(O, k_b=16, block=64, W=128):
         assert np.allclose(o, v.mean(axis=0)[None, :], rtol=0, atol=1e-12)
 
 
+def check_e4m3fn_encode(O):
+    """The E4M3FN encoder against torch's float8_e4m3fn conversion (a library routine): every
+    finite code value and its negative, every midpoint between neighbouring codes (ties to the
+    even code), random fp32 values in range; values past 448 saturate to +-448."""
+    codes = np.arange(0x7F, dtype=np.uint8)
+    vals = O.e4m3fn_bits_to_f64(codes)
+    assert np.array_equal(O.e4m3fn_encode_rne(vals), codes)
+    assert np.array_equal(O.e4m3fn_encode_rne(-vals[1:]), codes[1:] | 0x80)
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(12)
+    rnd = (rng.standard_normal(20000) * np.exp(rng.uniform(-9, 6, 20000))).astype(np.float32)
+    rnd = rnd[np.abs(rnd) <= 448]
+    for x in (mids, -mids, rnd.astype(np.float64)):
+        ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        assert np.array_equal(O.e4m3fn_encode_rne(x), ref)
+    assert O.e4m3fn_encode_rne(np.array([448.5, 1e6, -470.0])).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def check_bridge_fp8(O):
+    """Multi-target FP8 bridge: the codes equal torch's E4M3FN conversion of x / scale computed in
+    fp32 from an independent float64 product; every non-zero row reaches +-448; the decoded value is
+    within half an E4M3 step of the exact product; a zero row gets scale 1 and zero codes; a target
+    whose Wk is another target's Wv reproduces that V."""
+    rng = np.random.default_rng(13)
+    T, D, d = 41, 64, 16
+
+    def bits(a):
+        return torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+    def dec(u):
+        return torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+    h = bits(rng.standard_normal((T, D)))
+    h[5] = 0
+    wk = [bits(rng.standard_normal((d, D)) * 0.05) for _ in range(2)]
+    wv = [bits(rng.standard_normal((d, D)) * 0.05) for _ in range(2)]
+    wk[1] = wv[0].copy()
+    out = O.kv_bridge_fp8(h, wk, wv, row_block=16)
+    assert len(out) == 2
+    for tgt in range(2):
+        for (codes, scale), w in (((out[tgt][0], out[tgt][1]), wk[tgt]), ((out[tgt][2], out[tgt][3]), wv[tgt])):
+            x = torch.from_numpy(dec(h)) @ torch.from_numpy(dec(w)).T          # float64
+            x32 = x.float()
+            amax = x32.abs().amax(dim=1)
+            sc = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+            ref = (x32 / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert np.array_equal(codes, ref)
+            assert np.array_equal(scale, sc.numpy())
+            mags = np.max(codes & 0x7F, axis=1)
+            nz = amax.numpy() > 0
+            assert np.all(mags[nz] == 0x7E) and np.all(codes[~nz] == 0) and np.all(scale[~nz] == 1.0)
+            val = O.e4m3fn_bits_to_f64(codes) * scale.astype(np.float64)[:, None]
+            ex = x.numpy()
+            a = np.abs(ex) / scale.astype(np.float64)[:, None]
+            step = np.where(a < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3))
+            assert np.all(np.abs(val - ex) <= (0.5 * step + 1e-6 * a) * scale.astype(np.float64)[:, None] + 1e-12)
+    assert np.array_equal(out[1][0], out[0][2]) and np.array_equal(out[1][1], out[0][3])
+
+
 ALL_CHECKS = [check_dense_vs_sdpa, check_identical_keys, check_score_mass, check_onehot_keys,
               check_selection_bruteforce, check_selection_exhaustive, check_window_enumeration,
               check_sparse_identity, check_sparse_order_invariance, check_needles, check_bf16,
-              check_e4m3fn, check_bridge, check_block_selection, check_block_rows]
+              check_e4m3fn, check_bridge, check_block_selection, check_block_rows,
+              check_e4m3fn_encode, check_bridge_fp8]

@@ -63,6 +63,12 @@ MUTATIONS = [
      "np.arange(b * block, (b + 1) * block)"),
     ("blocks shifted by one position", "score[b * block: min(C, (b + 1) * block)]",
      "score[b * block + 1: min(C, (b + 1) * block + 1)]"),
+    ("e4m3 encoder ties to odd", "((d_hi == d_lo) & (hi % 2 == 0))", "((d_hi == d_lo) & (hi % 2 == 1))"),
+    ("fp8 scale from 240", "sc = (amax / np.float32(FP8_MAX)).astype(np.float32)",
+     "sc = (amax / np.float32(240.0)).astype(np.float32)"),
+    ("fp8 bridge projects V with Wk", "for w_b in (wk_b, wv_b):", "for w_b in (wk_b, wk_b):"),
+    ("fp8 bridge rounds x to bf16 first", "x = (h @ w.T).astype(np.float32)",
+     "x = f64_to_bf16_bits_rne(h @ w.T); x = bf16_bits_to_f64(x).astype(np.float32)"),
     ("sparse softmax without max shift cancels nothing but wrong normaliser",
      "p = e / e.sum(axis=1, keepdims=True)\n    return p @ v[sel]",
      "p = e / e.sum()\n    return p @ v[sel]"),
