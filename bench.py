@@ -96,6 +96,7 @@ KERNEL_UNITS = {
     "sparse_attn_layers_mfma": ("sparse_layers", "hbm"),
     "bridge_mfma": ("bridge", "hbm"),
     "bridge_rows": ("bridge", "hbm"),
+    "bridge_fp8": ("bridge_fp8", "mfma"),
 }
 KERNEL_SOURCES = {
     "full_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
@@ -104,6 +105,7 @@ KERNEL_SOURCES = {
     "sparse_attn_layers_mfma": ["attn_rows.hip", "mfma_tiles.h"],
     "bridge_mfma": ["bridge_mfma.hip", "mfma_tiles.h"],
     "bridge_rows": ["bridge_rows.hip"],
+    "bridge_fp8": ["bridge_fp8.hip"],
 }
 
 
@@ -375,6 +377,88 @@ def agentic_main(cfg, args):
     print(json.dumps(out), flush=True)
 
 
+def bridge_fp8_main(cfg, args):
+    """Multi-target FP8 bridge: a step is one hs2_kv_bridge_fp8 call, all targets' K/V caches of
+    cfg.T tokens projected from the same hidden states (resident in HBM) and quantised."""
+    import torch
+
+    import token_level_sparse_mqa_amd as hs2
+    from workloads import make_bridge_fp8_inputs
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {cfg.name}")
+    inp = make_bridge_fp8_inputs(cfg)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    hid = up(inp.hidden)
+    wks, wvs = [up(w) for w in inp.wk_t], [up(w) for w in inp.wv_t]
+    kc = [torch.empty((cfg.T, cfg.d), dtype=torch.uint8, device=dev) for _ in range(cfg.L)]
+    vc = [torch.empty((cfg.T, cfg.d), dtype=torch.uint8, device=dev) for _ in range(cfg.L)]
+    ks = [torch.empty((cfg.T,), dtype=torch.float32, device=dev) for _ in range(cfg.L)]
+    vs = [torch.empty((cfg.T,), dtype=torch.float32, device=dev) for _ in range(cfg.L)]
+
+    def step():
+        hs2.hs2_kv_bridge_fp8(hid, wks, wvs, k_outs=kc, v_outs=vc, k_scales=ks, v_scales=vs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(args.steps)
+    kernels = {}
+    if not args.no_profile:
+        hs2.profile_enable(True)
+        timed(args.steps)
+        for name, (tot, n) in hs2.profile_read().items():
+            kernels[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
+        hs2.profile_enable(False)
+    roof = None
+    if "bridge_fp8" in kernels:
+        ach = cfg.flops / (kernels["bridge_fp8"]["avg_us"] / 1e6) / 1e12
+        roof = {"bound": "mfma", "kernel": "bridge_fp8", "achieved": ach, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": ach / BF16_PEAK_TFLOPS, "traffic": stored_traffic(cfg.name, "bridge_fp8")}
+    hbm_bytes = cfg.T * cfg.D * 2 + cfg.L * 2 * (cfg.d * cfg.D * 2 + cfg.T * (cfg.d + 4))
+    out = {
+        "metric": "multi-target FP8 KV bridge: tokens/s projected into every target's FP8 cache",
+        "value": cfg.T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "hidden": cfg.D, "d": cfg.d, "targets": cfg.L,
+                   "output": "fp8 e4m3fn + fp32 row scale"},
+        "roofline": roof, "step_hbm_frac": hbm_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        log("[bench] cpu baseline (oracle)")
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:  # pragma: no cover
+            cores = len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < 10.0 and done < cfg.T:
+            oracle.kv_bridge_fp8(inp.hidden[done:done + 4096], inp.wk_t, inp.wv_t)
+            done += 4096
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": done / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                               "sample": f"the first {done} tokens of {cfg.name} (all {cfg.L} targets), {el:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
 def gather_cold_sweep(reps=5):
     """Supplementary, labelled measurement of the sparse-layer kernel on decode-shaped gathers
     large enough to be bandwidth-dominated: B sequences x 1 query x S = 1152 selected rows (a
@@ -490,9 +574,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    from workloads import AGENTIC, CONFIGS
+    from workloads import AGENTIC, BRIDGE_FP8, CONFIGS
     if args.workload in AGENTIC:
         agentic_main(AGENTIC[args.workload], args)
+        return
+    if args.workload in BRIDGE_FP8:
+        bridge_fp8_main(BRIDGE_FP8[args.workload], args)
         return
     cfg = CONFIGS[args.workload]
     if args.calib_copy_mib:

@@ -97,6 +97,33 @@ hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D,
                          hipStream_t stream);
 
 /*
+ * Multi-target KV Bridging into FP8 caches: every cross-decoder full-attention layer (target)
+ * projects the same self-decoder hidden states with its own projections (lynxflow "Two-Level KV
+ * Sharing"), and its cache is FP8 E4M3FN with a per-row fp32 scale (ainews experimental-setup
+ * paragraph).  For each target l = 0..L-1 and row t:
+ *   x[c] = sum_i hidden[t, i] * w_k[l][c, i]                     (fp32 accumulation)
+ *   k_scale[l][t] = max_c |x[c]| / 448   (1 when the row is all zero)
+ *   k_out[l][t * out_row_stride + c] = E4M3FN(x[c] / k_scale[l][t])   (nearest, ties to even,
+ *                                                                      saturating at +-448)
+ * and V likewise with w_v, v_out, v_scale.  The decoded cache row is code * scale.
+ *   hidden : bf16 [T, D] row-major
+ *   w_k, w_v : HOST arrays of L device pointers, each bf16 [d, D] (a linear layer's weight:
+ *              output row c holds that column's D weights)
+ *   k_out, v_out : HOST arrays of L device pointers to u8 codes; row t at byte t * out_row_stride
+ *   k_scale, v_scale : HOST arrays of L device pointers to fp32 [T]
+ * All targets are computed in one launch.  Targets whose hidden states differ (one source layer
+ * each) take one call per hidden buffer.
+ * Requirements: 1 <= L <= 8, T >= 0, D % 64 == 0, d in {64, 128}, out_row_stride >= d;
+ *   hidden and weights 16-byte aligned, scales 4-byte aligned.  T == 0 is a no-op.
+ *   Inputs are finite (a non-finite product gives unspecified codes).
+ */
+hs2_status hs2_kv_bridge_fp8(const void* hidden, int64_t T, int32_t D,
+                             const void* const* w_k, const void* const* w_v, int32_t L, int32_t d,
+                             void* const* k_out, void* const* v_out,
+                             float* const* k_scale, float* const* v_scale,
+                             int64_t out_row_stride, hipStream_t stream);
+
+/*
  * Bytes of workspace hs2_full_attn_select needs for these sizes (0 on invalid sizes).
  * The same value is valid for every call with sizes no larger than these and the same dtype.
  */

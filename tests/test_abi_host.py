@@ -198,3 +198,30 @@ def test_sparse_layers_workspace_size():
 ])
 def test_bridge_rejects(args, status):
     assert hs2.lib().hs2_kv_bridge(*args) == status
+
+
+def _b8(T=10, D=128, L=2, d=128, stride=128, hidden=FAKE, arrays=True, **slot):
+    def arr(v):
+        return ctypes.cast((ctypes.c_void_p * max(L, 1))(*([v] * max(L, 1))), ctypes.c_void_p) if arrays else None
+    return hs2.lib().hs2_kv_bridge_fp8(hidden, T, D, arr(slot.get("wk", FAKE)), arr(slot.get("wv", FAKE)), L, d,
+                                       arr(slot.get("ko", FAKE)), arr(slot.get("vo", FAKE)),
+                                       arr(slot.get("ks", FAKE)), arr(slot.get("vs", FAKE)), stride, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(L=9), hs2.HS2_ERR_INVALID_ARG),
+    (dict(D=100), hs2.HS2_ERR_INVALID_ARG),
+    (dict(d=96, stride=96), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(stride=64), hs2.HS2_ERR_INVALID_ARG),
+    (dict(arrays=False), hs2.HS2_ERR_INVALID_ARG),
+    (dict(hidden=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(hidden=FAKE + 8), hs2.HS2_ERR_INVALID_ARG),
+    (dict(wk=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(wv=FAKE + 2), hs2.HS2_ERR_INVALID_ARG),
+    (dict(ks=FAKE + 2), hs2.HS2_ERR_INVALID_ARG),
+    (dict(T=-1), hs2.HS2_ERR_INVALID_ARG),
+    (dict(T=0, hidden=None), hs2.HS2_OK),
+])
+def test_bridge_fp8_rejects(kw, status):
+    assert _b8(**kw) == status

@@ -4,7 +4,7 @@ Argument marshalling only: every step of the path runs in the HIP kernels of lib
 called through its C ABI (include/hs2.h) with ctypes.  torch provides device memory and
 the current stream.  The functions carry the C names:
 
-    hs2_kv_bridge, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
+    hs2_kv_bridge, hs2_kv_bridge_fp8, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
     hs2_full_attn_select_blocks, hs2_full_attn_select_blocks_workspace_size,
     hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_sparse_attn_layers,
     hs2_sparse_attn_layers_workspace_size, hs2_last_error, hs2_version
@@ -30,6 +30,7 @@ _vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ct
 
 _SIGS = {
     "hs2_kv_bridge": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp]),
+    "hs2_kv_bridge_fp8": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i64, _vp]),
     "hs2_full_attn_select_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_int]),
     "hs2_full_attn_select": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                             _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
@@ -131,6 +132,44 @@ def hs2_kv_bridge(hidden: torch.Tensor, w_k: torch.Tensor, w_v: torch.Tensor,
     _check(lib().hs2_kv_bridge(_ptr(hidden), T, D, _ptr(w_k), _ptr(w_v), d, k_out.data_ptr(),
                                v_out.data_ptr(), stride, _stream(stream)))
     return k_out, v_out
+
+
+def _ptr_array(ts):
+    return ctypes.cast((ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts]), ctypes.c_void_p)
+
+
+def hs2_kv_bridge_fp8(hidden: torch.Tensor, w_ks, w_vs, k_outs=None, v_outs=None, k_scales=None, v_scales=None,
+                      out_row_stride: Optional[int] = None, stream=None):
+    """Multi-target bridge into FP8 caches.  hidden [T, D] bf16; w_ks, w_vs: one [d, D] bf16 weight
+    (linear layout) per target.  Returns (k_codes, k_scales, v_codes, v_scales), lists of u8 [T, d]
+    and fp32 [T] tensors (or the given ones, which may be row views of wider caches)."""
+    T, D = hidden.shape
+    L = len(w_ks)
+    d = w_ks[0].shape[0]
+    dev = hidden.device
+    if len(w_vs) != L:
+        raise ValueError("one w_v per w_k")
+    for w in list(w_ks) + list(w_vs):
+        if w.shape != (d, D) or w.dtype != torch.bfloat16:
+            raise ValueError("weights must be bf16 [d, D]")
+    if k_outs is None:
+        k_outs = [torch.empty((T, d), dtype=torch.uint8, device=dev) for _ in range(L)]
+    if v_outs is None:
+        v_outs = [torch.empty((T, d), dtype=torch.uint8, device=dev) for _ in range(L)]
+    if k_scales is None:
+        k_scales = [torch.empty((T,), dtype=torch.float32, device=dev) for _ in range(L)]
+    if v_scales is None:
+        v_scales = [torch.empty((T,), dtype=torch.float32, device=dev) for _ in range(L)]
+    stride = d if out_row_stride is None else out_row_stride
+    for t in list(k_outs) + list(v_outs):
+        if t.dim() != 2 or t.shape != (T, d) or t.stride(1) != 1 or (T > 1 and t.stride(0) != stride):
+            raise ValueError("code outputs must be [T, d] u8 views with unit column stride and row stride "
+                             "out_row_stride")
+    _check(lib().hs2_kv_bridge_fp8(_ptr(hidden), T, D, _ptr_array(w_ks), _ptr_array(w_vs), L, d,
+                                   ctypes.cast((ctypes.c_void_p * L)(*[t.data_ptr() for t in k_outs]), ctypes.c_void_p),
+                                   ctypes.cast((ctypes.c_void_p * L)(*[t.data_ptr() for t in v_outs]), ctypes.c_void_p),
+                                   _ptr_array(k_scales), _ptr_array(v_scales), stride, _stream(stream)))
+    return k_outs, k_scales, v_outs, v_scales
 
 
 def hs2_full_attn_select_workspace_size(B: int, Tq: int, H: int, d: int, Nmax: int, k_global: int,

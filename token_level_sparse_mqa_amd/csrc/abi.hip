@@ -238,6 +238,39 @@ hs2_status hs2_kv_bridge(const void* hidden, int64_t T, int32_t D, const void* w
     return HS2_OK;
 }
 
+hs2_status hs2_kv_bridge_fp8(const void* hidden, int64_t T, int32_t D, const void* const* w_k,
+                             const void* const* w_v, int32_t L, int32_t d, void* const* k_out, void* const* v_out,
+                             float* const* k_scale, float* const* v_scale, int64_t out_row_stride,
+                             hipStream_t stream) {
+    if (T < 0) return fail(HS2_ERR_INVALID_ARG, "T must be >= 0");
+    if (L < 1 || L > kMaxTargets) return fail(HS2_ERR_INVALID_ARG, "L=%d outside [1, %d]", L, kMaxTargets);
+    if (D < 1 || D % 64 != 0) return fail(HS2_ERR_INVALID_ARG, "D=%d must be a positive multiple of 64", D);
+    if (d != 64 && d != 128) return fail(HS2_ERR_UNSUPPORTED, "d=%d not supported (64 or 128)", d);
+    if (out_row_stride < d) return fail(HS2_ERR_INVALID_ARG, "out_row_stride %lld < d", (long long)out_row_stride);
+    if (!w_k || !w_v || !k_out || !v_out || !k_scale || !v_scale)
+        return fail(HS2_ERR_INVALID_ARG, "null pointer array");
+    if (T == 0) return HS2_OK;
+    if (!hidden || !aligned(hidden, 16)) return fail(HS2_ERR_INVALID_ARG, "hidden must be non-null and 16-byte aligned");
+    BridgeFp8Args a{};
+    a.hidden = (const uint16_t*)hidden; a.T = T; a.D = D; a.d = d; a.L = L; a.stride = out_row_stride;
+    for (int l = 0; l < L; ++l) {
+        if (!w_k[l] || !w_v[l] || !k_out[l] || !v_out[l] || !k_scale[l] || !v_scale[l])
+            return fail(HS2_ERR_INVALID_ARG, "null pointer for target %d", l);
+        if (!aligned(w_k[l], 16) || !aligned(w_v[l], 16) || !aligned(k_scale[l], 4) || !aligned(v_scale[l], 4))
+            return fail(HS2_ERR_INVALID_ARG, "target %d: weights must be 16-byte and scales 4-byte aligned", l);
+        a.wk[l] = (const uint16_t*)w_k[l]; a.wv[l] = (const uint16_t*)w_v[l];
+        a.k_out[l] = (uint8_t*)k_out[l]; a.v_out[l] = (uint8_t*)v_out[l];
+        a.k_scale[l] = k_scale[l]; a.v_scale[l] = v_scale[l];
+    }
+    for (int l = L; l < kMaxTargets; ++l) {      // unused slots repeat target 0 (never selected)
+        a.wk[l] = a.wk[0]; a.wv[l] = a.wv[0]; a.k_out[l] = a.k_out[0]; a.v_out[l] = a.v_out[0];
+        a.k_scale[l] = a.k_scale[0]; a.v_scale[l] = a.v_scale[0];
+    }
+    hipError_t e = launch_bridge_fp8(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_bridge_fp8 launch");
+    return HS2_OK;
+}
+
 size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
                                            int32_t k_global, int32_t window, hs2_dtype kv_dtype) {
     (void)window;

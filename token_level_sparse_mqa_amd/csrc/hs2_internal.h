@@ -84,6 +84,16 @@ struct BridgeArgs {
     uint16_t* k_out; uint16_t* v_out; int64_t stride;
 };
 
+constexpr int kMaxTargets = 8;       // target layers of one multi-target bridge launch
+
+struct BridgeFp8Args {
+    const uint16_t* hidden; int64_t T; int D; int d; int L;
+    const uint16_t* wk[kMaxTargets]; const uint16_t* wv[kMaxTargets];    // [d, D] each
+    uint8_t* k_out[kMaxTargets]; uint8_t* v_out[kMaxTargets];            // row t at t * stride bytes
+    float* k_scale[kMaxTargets]; float* v_scale[kMaxTargets];            // [T]
+    int64_t stride;
+};
+
 // Kernel launchers (return the launch status).
 hipError_t launch_attn_generic(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t s);
@@ -93,6 +103,7 @@ hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t s);
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s);
 bool bridge_rows_fits(const BridgeArgs& a);
 hipError_t launch_bridge_rows(const BridgeArgs& a, hipStream_t s);
+hipError_t launch_bridge_fp8(const BridgeFp8Args& a, hipStream_t s);
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_rows_mfma(const ScoreArgs& a, hipStream_t s);

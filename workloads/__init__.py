@@ -9,3 +9,4 @@ path consume the bytes produced here.
 from .configs import CONFIGS, Config, get_config, small_config  # noqa: F401
 from .gen import Workload, make_workload  # noqa: F401
 from .agentic import AGENTIC, AgenticConfig, AgenticInputs, make_agentic  # noqa: F401
+from .bridge_fp8 import BRIDGE_FP8, BridgeFp8Config, BridgeFp8Inputs, make_bridge_fp8_inputs  # noqa: F401
