@@ -135,3 +135,28 @@ def test_bridge_fp8_full_size_sampled():
     # compare the sampled rows: the oracle ran on those rows only
     got_rows = [(g[0][rows], g[1][rows], g[2][rows], g[3][rows]) for g in got]
     check_fp8_close(sub, inp.wk_t, inp.wv_t, got_rows, ref)
+
+
+def test_bridge_fp8_encoder_exact():
+    """The conversion to E4M3FN on its own: one-hot hidden rows pick a weight column per row, and a
+    448 in column 0 makes every row's scale exactly 1, so each code is the encoding of a chosen bf16
+    value: every midpoint between neighbouring codes (ties to even), every code value, random values
+    in range, both signs; bit-identical to the oracle's encoder."""
+    T, D, d = 64, 64, 128
+    vals = oracle.e4m3fn_bits_to_f64(np.arange(0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    rng = np.random.default_rng(21)
+    pool = np.concatenate([vals, mids, -vals, -mids, rng.uniform(-448, 448, 4096)])
+    pool = oracle.bf16_bits_to_f64(f32_to_bf16_bits(pool.astype(np.float32)))    # bf16 values (mids exact)
+    need = T * (d - 1)
+    pool = np.resize(rng.permutation(pool), need)
+    w = np.zeros((d, D), dtype=np.float32)
+    w[0, :] = 448.0
+    w[1:, :T] = pool.reshape(d - 1, T)
+    wb = f32_to_bf16_bits(w)
+    hb = f32_to_bf16_bits(np.eye(T, D, dtype=np.float32))
+    got = _host(_run(hb, [wb], [wb[::-1].copy()]))
+    ref = oracle.kv_bridge_fp8(hb, [wb], [wb[::-1].copy()])
+    assert np.all(got[0][1] == 1.0)
+    for a, b, what in zip(got[0], ref[0], ("k codes", "k scale", "v codes", "v scale")):
+        assert np.array_equal(a, b), what

@@ -16,7 +16,8 @@
 // both MFMA operands are 8 consecutive reduction elements of one LDS row, read at full rate with
 // ds_read_b128 (rows of 128 bytes, 16-byte chunks XOR-swizzled by row pair).  Eight waves in a
 // 4 x 2 grid hold 64 rows x d columns each (K for wave column 0, V for 1), so a wave holds whole
-// K or V rows and the per-row maximum is a fold over its own lanes.  The reduction runs in
+// K or V rows and the per-row maximum is a fold over its own lanes.  The codes come from the
+// packed fp32 -> E4M3FN conversion (nearest, ties to even), two per instruction.  The reduction runs in
 // 64-deep chunks, double-buffered in LDS with the next chunk's loads in flight in registers.
 #include "hs2_device.h"
 #include "mfma_tiles.h"
@@ -34,23 +35,6 @@ constexpr int kB8Stages = 2;
 // chunk index is XORed with the row pair number; 16 consecutive rows read at one chunk then hit
 // 16 different bank groups.
 __device__ __forceinline__ int b8_off(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
-
-// OCP E4M3FN code of a finite fp32 value: nearest, ties to even, saturating at +-448.
-__device__ __forceinline__ uint32_t f32_to_e4m3fn_sat(float y) {
-    const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-    const float a = fabsf(y);
-    uint32_t code;
-    if (!(a < 448.0f)) {
-        code = 0x7Eu;
-    } else if (a < 0.015625f) {                  // below 2^-6: multiples of 2^-9 (exact scaling)
-        code = (uint32_t)__builtin_rintf(a * 512.0f);
-    } else {                                     // keep 3 mantissa bits, round on the 20 dropped
-        uint32_t u = __float_as_uint(a);
-        u += 0x7FFFFu + ((u >> 20) & 1u);
-        code = (u >> 20) - ((127u - 7u) << 3);
-    }
-    return code | sign;
-}
 
 template <int DD>
 __global__ __launch_bounds__(kB8Threads, 1) void bridge_fp8_kernel(BridgeFp8Args a) {
@@ -178,14 +162,26 @@ __global__ __launch_bounds__(kB8Threads, 1) void bridge_fp8_kernel(BridgeFp8Args
 #pragma unroll
             for (int s = 1; s < 32; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
             const float scale = m > 0.f ? __fdiv_rn(m, 448.0f) : 1.0f;
+            // x / scale rounded to nearest: one correctly rounded reciprocal per row, then per
+            // element q = x r and one correction with the exact residual x - q scale (Markstein)
+            const float r = __fdiv_rn(1.0f, scale);
             const int64_t row = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * hb + (e & 3);
+            float y[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const float x = acc[i][j][e];
+                const float q = x * r;
+                y[j] = fmaf(fmaf(-q, scale, x), r, q);
+            }
+            // E4M3FN codes (nearest, ties to even) of columns 32 j + n, byte j of pk
+            uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+            if constexpr (NB == 4) pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)pk, true);
             if (row < a.T) {
                 uint8_t* orow = out + row * a.stride;
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    orow[32 * j + n] = (uint8_t)f32_to_e4m3fn_sat(__fdiv_rn(acc[i][j][e], scale));
-                if (n == 0) sout[row] = scale;
+                for (int j = 0; j < NB; ++j) orow[32 * j + n] = (uint8_t)(pk >> (8 * j));
             }
+            if (row < a.T && n == 0) sout[row] = scale;
         }
 }
 
