@@ -574,14 +574,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    from workloads import AGENTIC, BRIDGE_FP8, CONFIGS
-    if args.workload in AGENTIC:
-        agentic_main(AGENTIC[args.workload], args)
-        return
-    if args.workload in BRIDGE_FP8:
-        bridge_fp8_main(BRIDGE_FP8[args.workload], args)
-        return
-    cfg = CONFIGS[args.workload]
     if args.calib_copy_mib:
         import torch
         src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda:0")
@@ -590,6 +582,14 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    from workloads import AGENTIC, BRIDGE_FP8, CONFIGS
+    if args.workload in AGENTIC:
+        agentic_main(AGENTIC[args.workload], args)
+        return
+    if args.workload in BRIDGE_FP8:
+        bridge_fp8_main(BRIDGE_FP8[args.workload], args)
+        return
+    cfg = CONFIGS[args.workload]
     res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile, select=args.select)
     ms = res["ms_per_step"]
     value = res["rows"] / (ms / 1e3)
