@@ -97,6 +97,7 @@ KERNEL_UNITS = {
     "bridge_mfma": ("bridge", "hbm"),
     "bridge_rows": ("bridge", "hbm"),
     "bridge_fp8": ("bridge_fp8", "mfma"),
+    "decode_block": ("step", "hbm"),
 }
 KERNEL_SOURCES = {
     "full_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
@@ -134,7 +135,7 @@ def stored_traffic(workload, kernel):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def run_gpu(cfg, steps, warmup, profile=True, select="token"):
+def run_gpu(cfg, steps, warmup, profile=True, select="token", decode_block=False):
     import torch
 
     import token_level_sparse_mqa_amd as hs2
@@ -162,9 +163,19 @@ def run_gpu(cfg, steps, warmup, profile=True, select="token"):
     idx = torch.empty((cfg.B, cfg.Tq, cfg.S), dtype=torch.int32, device=dev)
     o_sp = [torch.empty_like(o) for _ in range(cfg.n_sparse)]
 
+    if decode_block:
+        dbws = hs2.decode_block_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global, cfg.window, kvd,
+                                          cfg.n_sparse, dev)
+
     def step():
         if cfg.bridge_D:
             hs2.hs2_kv_bridge(t["hidden"], t["wk"], t["wv"], k_out=t["k"][0], v_out=t["v"][0])
+        if decode_block:
+            # the whole block (full layer, selection, sparse layers) in one launch
+            hs2.hs2_decode_block(t["q"], t["qs"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
+                                 v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
+                                 o=o, idx=idx, os=o_sp, workspace=dbws)
+            return
         if blocks:
             hs2.hs2_full_attn_select_blocks(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
                                             v_scale=t["v_scale"], k_blocks=kb, block=BLOCK, window=cfg.window,
@@ -560,6 +571,8 @@ def main():
     ap.add_argument("--workload", default="decode128k")
     ap.add_argument("--select", choices=("token", "blocks"), default="token",
                     help="token-level selection (the method) or the 64-token block-level variant")
+    ap.add_argument("--decode-block", action="store_true",
+                    help="decode workloads: run the hybrid block as one launch (hs2_decode_block)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-gather-sweep", action="store_true",
@@ -590,7 +603,8 @@ def main():
         bridge_fp8_main(BRIDGE_FP8[args.workload], args)
         return
     cfg = CONFIGS[args.workload]
-    res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile, select=args.select)
+    res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile, select=args.select,
+                  decode_block=args.decode_block)
     ms = res["ms_per_step"]
     value = res["rows"] / (ms / 1e3)
     alg = algorithmic(cfg)
@@ -623,7 +637,8 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "context": cfg.N, "Tq": cfg.Tq, "H": cfg.H, "d": cfg.d,
                    "kv_dtype": cfg.kv_dtype, "k_global": cfg.k_global, "window": cfg.window,
                    "sparse_layers": cfg.n_sparse, "bridge_D": cfg.bridge_D,
-                   "selection": "token" if args.select == "token" else f"blocks of {BLOCK}"},
+                   "selection": "token" if args.select == "token" else f"blocks of {BLOCK}",
+                   "launch": "one launch (hs2_decode_block)" if args.decode_block else "one launch per kernel"},
         "roofline": roof, "step_roofline_frac": step_frac, "kernels": kernels,
     }
     if cfg.Tq == 1 and not args.no_gather_sweep and not args.no_profile:

@@ -192,6 +192,42 @@ hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype,
                                        hipStream_t stream);
 
 /*
+ * Bytes of workspace hs2_decode_block needs for these sizes (0 on invalid sizes).
+ */
+size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                       int32_t k_global, int32_t window, hs2_dtype kv_dtype, int32_t L);
+
+/*
+ * The decode hybrid block in one launch: the full-attention layer with token-level selection
+ * (exactly hs2_full_attn_select) followed by L sparse layers on the indices it selected (exactly
+ * hs2_sparse_attn_layers with a workspace), as one cooperative kernel launch whose phases are
+ * separated by grid-wide barriers (lynxflow "Two-Level KV Sharing": the sparse layers reuse the
+ * full layer's cache and indices; ainews page: latency depends on kernel efficiency, data
+ * movement and scheduling).
+ *   q : bf16 [B, Tq, H, d] (the full layer's queries); q_sparse : HOST array of L device pointers
+ *   to bf16 [B, Tq, H, d]; o : fp32 [B, Tq, H, d]; idx : int32 [B, Tq, k_global + window];
+ *   o_sparse : HOST array of L device pointers to fp32 [B, Tq, H, d].  Everything else as for
+ *   hs2_full_attn_select.
+ * Results are bit-identical to the two separate calls.  On MI355X the separate calls are faster
+ * (phase boundaries inside one launch need device-wide barriers and cache write-back and
+ * invalidation that kernel boundaries provide for free); this entry point is for callers that
+ * need the block as a single launch.
+ * Requirements: bf16 queries, decode rows (Tq < 8), 1 <= L <= 8, k_global + window small enough
+ *   for one sparse split (at most 1280 rows per split), workspace_bytes >=
+ *   hs2_decode_block_workspace_size(...).  The launch needs every workgroup resident at once:
+ *   the GPU must not be shared with work that holds compute units for the duration (the
+ *   runtime rejects a cooperative launch that cannot fit, with HS2_ERR_HIP).
+ */
+hs2_status hs2_decode_block(const void* q, const void* const* q_sparse, int32_t L, hs2_dtype q_dtype,
+                            const void* k, const void* v, hs2_dtype kv_dtype,
+                            const float* k_scale, const float* v_scale,
+                            const int32_t* q_pos, const int32_t* kv_len,
+                            int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                            int32_t k_global, int32_t window, float sm_scale,
+                            float* o, int32_t* idx, float* const* o_sparse,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Sparse (index-reusing) attention layer (KV Reuse).
  *   o[b,i,h] = sum_{j in sel} softmax_j(sm_scale * q_h . k_j) v_j,
  *   sel = { idx[b,i,e] : 0 <= e < S, 0 <= idx[b,i,e] < min(kv_len[b], Nmax) }.

@@ -225,3 +225,43 @@ def _b8(T=10, D=128, L=2, d=128, stride=128, hidden=FAKE, arrays=True, **slot):
 ])
 def test_bridge_fp8_rejects(kw, status):
     assert _b8(**kw) == status
+
+
+def _db(L=2, qarr=True, oarr=True, **kw):
+    a = dict(q=FAKE, qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, qp=FAKE, kl=FAKE,
+             B=1, Tq=1, H=32, d=128, N=4096, kg=1024, W=128, sm=0.088, o=FAKE, idx=FAKE, ws=FAKE, wsb=1 << 40)
+    a.update(kw)
+    n = max(L, 1)
+    qa = ctypes.cast((ctypes.c_void_p * n)(*([kw.get("qs", FAKE)] * n)), ctypes.c_void_p) if qarr else None
+    oa = ctypes.cast((ctypes.c_void_p * n)(*([kw.get("os", FAKE)] * n)), ctypes.c_void_p) if oarr else None
+    return hs2.lib().hs2_decode_block(a["q"], qa, L, a["qd"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"], a["qp"],
+                                      a["kl"], a["B"], a["Tq"], a["H"], a["d"], a["N"], a["kg"], a["W"], a["sm"],
+                                      a["o"], a["idx"], oa, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Tq=8), hs2.HS2_ERR_UNSUPPORTED),            # query chunks: the separate calls
+    (dict(qd=hs2.HS2_F32, kvd=hs2.HS2_F32), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(L=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(L=9), hs2.HS2_ERR_INVALID_ARG),
+    (dict(qarr=False), hs2.HS2_ERR_INVALID_ARG),
+    (dict(oarr=False), hs2.HS2_ERR_INVALID_ARG),
+    (dict(qs=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(os=FAKE + 4), hs2.HS2_ERR_INVALID_ARG),
+    (dict(B=300, kg=2048, W=128), hs2.HS2_ERR_UNSUPPORTED),    # unsplit rows of 2176 entries
+    (dict(idx=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(ws=None), hs2.HS2_ERR_WORKSPACE),
+    (dict(wsb=1024), hs2.HS2_ERR_WORKSPACE),
+    (dict(B=0), hs2.HS2_OK),
+])
+def test_decode_block_rejects(kw, status):
+    assert _db(**kw) == status
+
+
+def test_decode_block_workspace_size():
+    full = hs2.hs2_full_attn_select_workspace_size(8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16)
+    both = hs2.hs2_decode_block_workspace_size(8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16, 3)
+    # the token-level plan plus the sparse layers' split partials (3 layers x 8 rows x 9 splits x 32 heads)
+    assert both >= full + 3 * 8 * 9 * 32 * 130 * 4
+    assert hs2.hs2_decode_block_workspace_size(8, 8, 32, 128, 131072, 1024, 128, hs2.HS2_BF16, 3) == 0
+    assert hs2.hs2_decode_block_workspace_size(8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16, 0) == 0

@@ -7,7 +7,8 @@ the current stream.  The functions carry the C names:
     hs2_kv_bridge, hs2_kv_bridge_fp8, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
     hs2_full_attn_select_blocks, hs2_full_attn_select_blocks_workspace_size,
     hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_sparse_attn_layers,
-    hs2_sparse_attn_layers_workspace_size, hs2_last_error, hs2_version
+    hs2_sparse_attn_layers_workspace_size, hs2_decode_block, hs2_decode_block_workspace_size,
+    hs2_last_error, hs2_version
 
 There is no fallback: if the built library is missing, loading raises.
 """
@@ -47,6 +48,10 @@ _SIGS = {
                                               _i32, _vp, _i32, _i32, _i32, _i32, _i64, _f32, _vp, _vp, _sz,
                                               _vp]),
     "hs2_sparse_attn_layers_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "hs2_decode_block_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32, _i32, ctypes.c_int, _i32]),
+    "hs2_decode_block": (ctypes.c_int, [_vp, _vp, _i32, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                        _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32, _vp, _vp, _vp, _vp, _sz,
+                                        _vp]),
     "hs2_last_error": (ctypes.c_char_p, []),
     "hs2_version": (ctypes.c_char_p, []),
     "hs2_profile_enable": (None, [ctypes.c_int]),
@@ -304,6 +309,52 @@ def hs2_sparse_attn_layers(qs, k: torch.Tensor, v: torch.Tensor, idx: torch.Tens
         _ptr(v_scale), _ptr(idx), S, _ptr(kv_len), B, Tq, H, d, Nmax, float(sm_scale),
         ctypes.cast(oa, ctypes.c_void_p), _ptr(workspace), wsb, _stream(stream)))
     return os
+
+
+def hs2_decode_block_workspace_size(B: int, Tq: int, H: int, d: int, Nmax: int, k_global: int, window: int,
+                                    kv_dtype: int, L: int) -> int:
+    return int(lib().hs2_decode_block_workspace_size(B, Tq, H, d, Nmax, k_global, window, kv_dtype, L))
+
+
+def decode_block_workspace(B: int, Tq: int, H: int, d: int, Nmax: int, k_global: int, window: int, kv_dtype: int,
+                           L: int, device) -> torch.Tensor:
+    n = hs2_decode_block_workspace_size(B, Tq, H, d, Nmax, k_global, window, kv_dtype, L)
+    return torch.empty((max(n, 1),), dtype=torch.uint8, device=device)
+
+
+def hs2_decode_block(q: torch.Tensor, qs, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+                     kv_len: torch.Tensor, k_scale: Optional[torch.Tensor] = None,
+                     v_scale: Optional[torch.Tensor] = None, k_global: int = 1024, window: int = 128,
+                     sm_scale: Optional[float] = None, o: Optional[torch.Tensor] = None,
+                     idx: Optional[torch.Tensor] = None, os=None, workspace: Optional[torch.Tensor] = None,
+                     stream=None):
+    """The decode hybrid block (full layer + selection + every sparse layer) in one launch.
+    Returns (o fp32 [B,Tq,H,d], idx int32 [B,Tq,k+W], [o of each sparse layer])."""
+    B, Tq, H, d = q.shape
+    L = len(qs)
+    Nmax = k.shape[1]
+    kvd = dtype_code(k)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
+    if idx is None:
+        idx = torch.empty((B, Tq, k_global + window), dtype=torch.int32, device=q.device)
+    if os is None:
+        os = [torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device) for _ in range(L)]
+    if workspace is None:
+        workspace = decode_block_workspace(B, Tq, H, d, Nmax, k_global, window, kvd, L, q.device)
+    for x in qs:
+        if x.shape != q.shape or x.dtype != q.dtype:
+            raise ValueError("every sparse layer's queries must have the full layer's shape and dtype")
+    qa = (ctypes.c_void_p * L)(*[_ptr(x) for x in qs])
+    oa = (ctypes.c_void_p * L)(*[_ptr(x) for x in os])
+    _check(lib().hs2_decode_block(
+        _ptr(q), ctypes.cast(qa, ctypes.c_void_p), L, dtype_code(q), _ptr(k), _ptr(v), kvd, _ptr(k_scale),
+        _ptr(v_scale), _ptr(q_pos), _ptr(kv_len), B, Tq, H, d, Nmax, k_global, window, float(sm_scale), _ptr(o),
+        _ptr(idx), ctypes.cast(oa, ctypes.c_void_p), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+    return o, idx, os
 
 
 def profile_enable(enable: bool = True):

@@ -424,6 +424,103 @@ hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype, const v
     return HS2_OK;
 }
 
+// ---- the decode hybrid block in one launch ------------------------------------------------------
+
+namespace {
+
+struct DecodeBlockPlan {
+    SelectPlan sel;
+    int sp_nsplit; int64_t sp_chunk;
+    size_t off_sparse, total;
+};
+
+DecodeBlockPlan plan_decode_block(int B, int Tq, int H, int d, int64_t Nmax, int k_global, int window,
+                                  int kv_dtype, int L) {
+    DecodeBlockPlan p{};
+    p.sel = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
+    const int64_t R = (int64_t)B * Tq;
+    const int S = k_global + window;
+    sparse_plan(R, S, HS2_BF16, &p.sp_nsplit, &p.sp_chunk);
+    p.off_sparse = p.sel.total;
+    const size_t sp = p.sp_nsplit > 1 ? (size_t)L * R * p.sp_nsplit * H * (d + 2) * 4 : 0;
+    p.total = p.off_sparse + align_up(sp);
+    return p;
+}
+
+}  // namespace
+
+size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                       int32_t k_global, int32_t window, hs2_dtype kv_dtype, int32_t L) {
+    if (B < 0 || Tq < 0 || Tq >= kPrefillMinTq || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 ||
+        k_global < 1 || k_global > 4096 || window < 0 || window > 4096 || L < 1 || L > kMaxLayers)
+        return 0;
+    if ((int64_t)B * Tq == 0) return kAlign;
+    return plan_decode_block(B, Tq, H, d, Nmax, k_global, window, kv_dtype, L).total;
+}
+
+hs2_status hs2_decode_block(const void* q, const void* const* q_sparse, int32_t L, hs2_dtype q_dtype,
+                            const void* k, const void* v, hs2_dtype kv_dtype, const float* k_scale,
+                            const float* v_scale, const int32_t* q_pos, const int32_t* kv_len, int32_t B,
+                            int32_t Tq, int32_t H, int32_t d, int64_t Nmax, int32_t k_global, int32_t window,
+                            float sm_scale, float* o, int32_t* idx, float* const* o_sparse, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st != HS2_OK) return st;
+    if (q_dtype != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "the single-launch block takes bf16 queries");
+    if (Tq >= kPrefillMinTq) return fail(HS2_ERR_UNSUPPORTED, "Tq=%d: the single-launch block is for decode rows (Tq < %d)", Tq, kPrefillMinTq);
+    if (!q_sparse || !o_sparse) return fail(HS2_ERR_INVALID_ARG, "null q_sparse or o_sparse pointer array");
+    if (L < 1 || L > kMaxLayers) return fail(HS2_ERR_INVALID_ARG, "L=%d outside [1, %d]", L, kMaxLayers);
+    if (k_global < 1 || k_global > 4096) return fail(HS2_ERR_INVALID_ARG, "k_global=%d outside [1, 4096]", k_global);
+    if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
+    for (int l = 0; l < L; ++l) {
+        st = check_common(q_sparse[l], q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o_sparse[l]);
+        if (st != HS2_OK) return st;
+    }
+    if ((int64_t)B * Tq == 0) return HS2_OK;
+    if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
+    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(workspace, 16))
+        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx must be 4-byte and the workspace 16-byte aligned");
+    const DecodeBlockPlan p = plan_decode_block(B, Tq, H, d, Nmax, k_global, window, kv_dtype, L);
+    if (p.sp_chunk > 1280)     // list entries one workgroup of the row kernel stages
+        return fail(HS2_ERR_UNSUPPORTED, "k_global + window = %d: a sparse split holds at most 1280 rows", k_global + window);
+    if (!workspace || workspace_bytes < p.total)
+        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
+    char* ws = (char*)workspace;
+    const int64_t R = (int64_t)B * Tq;
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
+    DecodeBlockArgs a{};
+    // full layer, as hs2_full_attn_select's row path
+    AttnArgs& f = a.full;
+    f.q = q; f.q_dtype = q_dtype; f.k = k; f.v = v; f.kv_dtype = kv_dtype; f.k_scale = k_scale; f.v_scale = v_scale;
+    f.q_pos = q_pos; f.kv_len = kv_len; f.list = nullptr; f.S = 0; f.B = B; f.Tq = Tq; f.H = H; f.d = d; f.Nmax = Nmax;
+    f.scale_log2 = scale_log2; f.nsplit = p.sel.nsplit; f.chunk = p.sel.chunk;
+    f.part = p.sel.nsplit > 1 ? (float*)(ws + p.sel.off_part) : nullptr;
+    f.part_ml = f.part ? f.part + R * p.sel.nsplit * H * d : nullptr;
+    f.o = o; f.lse = (float*)(ws + p.sel.off_lse); f.nlayer = 1;
+    f.zero_hist = (uint32_t*)(ws + p.sel.off_hist); f.zero_cnt = (uint32_t*)(ws + p.sel.off_cnt);
+    ScoreArgs& sa = a.score;
+    sa.q = q; sa.q_dtype = q_dtype; sa.k = k; sa.kv_dtype = kv_dtype; sa.k_scale = k_scale; sa.q_pos = q_pos;
+    sa.kv_len = kv_len; sa.B = B; sa.Tq = Tq; sa.H = H; sa.d = d; sa.Nmax = Nmax; sa.window = window;
+    sa.scale_log2 = scale_log2; sa.lse = f.lse; sa.scores = (float*)(ws + p.sel.off_scores); sa.cstride = Nmax;
+    sa.nsplit = p.sel.score_nsplit; sa.chunk = p.sel.score_chunk; sa.rowhist = f.zero_hist;
+    a.sel = select_args(p.sel, ws, q_pos, kv_len, Tq, Nmax, k_global, window, idx, nullptr);
+    // sparse layers, as hs2_sparse_attn_layers' split MFMA path over the indices just written
+    AttnArgs& sp = a.sparse;
+    sp.q = q_sparse[0]; sp.q_dtype = q_dtype; sp.k = k; sp.v = v; sp.kv_dtype = kv_dtype; sp.k_scale = k_scale;
+    sp.v_scale = v_scale; sp.q_pos = nullptr; sp.kv_len = kv_len; sp.list = idx; sp.S = k_global + window;
+    sp.B = B; sp.Tq = Tq; sp.H = H; sp.d = d; sp.Nmax = Nmax; sp.scale_log2 = scale_log2;
+    sp.nsplit = p.sp_nsplit; sp.chunk = p.sp_chunk; sp.nlayer = L;
+    for (int l = 0; l < L; ++l) { sp.ql[l] = q_sparse[l]; sp.ol[l] = o_sparse[l]; }
+    sp.o = o_sparse[0]; sp.lse = nullptr;
+    sp.part_lstride = R * p.sp_nsplit * H * d;
+    sp.ml_lstride = R * p.sp_nsplit * H * 2;
+    sp.part = p.sp_nsplit > 1 ? (float*)(ws + p.off_sparse) : nullptr;
+    sp.part_ml = sp.part ? sp.part + L * sp.part_lstride : nullptr;
+    hipError_t e = launch_decode_block(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "decode block launch");
+    return HS2_OK;
+}
+
 size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S) {
     if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || S < 1 || S > 8192) return 0;
     // the workspace is sized for the larger of the fp32 and bf16 plans

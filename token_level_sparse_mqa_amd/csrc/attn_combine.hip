@@ -1,137 +1,19 @@
-// Merge of the key splits of the row attention kernel: o = sum_s 2^(m_s - M) o_s / L with
-// M = max_s m_s and L = sum_s 2^(m_s - M) l_s per (row, head), from the MFMA partial layout
-// part [R, nsplit, H, d] (unnormalised o) and part_ml [R, nsplit, H, 2] (m, l; base 2).
-#include "hs2_device.h"
+// Device code of the split merge: attn_combine_dev.h (shared with the single-launch decode block).
+#include "attn_combine_dev.h"
 
 namespace hs2 {
 
-constexpr int kCombineNarrowMax = 32;  // splits up to which a (row, head) workgroup merges alone
-
-// The row of a workgroup and its buffers (multi-layer launches: block row x is row x % R of
-// layer x / R).
-struct CombineRow {
-    int r;
-    const float* part;
-    const float* part_ml;
-    float* o;
-    float* lse;
-};
-__device__ __forceinline__ CombineRow combine_row(const AttnArgs& a) {
-    CombineRow c{(int)blockIdx.x, a.part, a.part_ml, a.o, a.lse};
-    if (a.nlayer > 1) {
-        const int R = a.B * a.Tq, layer = c.r / R;
-        c.r -= layer * R;
-        c.part += layer * a.part_lstride;
-        c.part_ml += layer * a.ml_lstride;
-        c.o = a.ol[layer];
-        c.lse = nullptr;
-    }
-    return c;
-}
-
-// ---- merge of the splits of each row ----------------------------------------------------------------
-// Many splits (long rows): grid (row, head, D/16), 256 threads = 16 dims x 16 split lanes.  Every
-// workgroup first reduces the per-split maxima and sums of its head (tiny), then sums its 16
-// dims over the splits.
+// Many splits (long rows): grid (row, head, D/16), 256 threads = 16 dims x 16 split lanes.
 template <int D>
 __global__ __launch_bounds__(256) void attn_split_combine_wide_kernel(AttnArgs a) {
-    __shared__ float red[16][17];
-    __shared__ float wred[4];
-    const CombineRow cr = combine_row(a);
-    const int r = cr.r, h = blockIdx.y, H = a.H, ns = a.nsplit;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // split s: o at obase + s * ostride, (m, l) at mbase + s * mstride
-    const float* obase = cr.part + ((int64_t)r * ns * H + h) * D;
-    const float* mbase = cr.part_ml + ((int64_t)r * ns * H + h) * 2;
-    const int64_t ostride = (int64_t)H * D, mstride = (int64_t)H * 2;
-    float m = kNegInf;
-    for (int s = tid; s < ns; s += 256) m = fmaxf(m, mbase[s * mstride]);
-    m = wave_max(m);
-    if (lane == 0) wred[wv] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-    __syncthreads();
-    float l = 0.f;
-    if (M != kNegInf)
-        for (int s = tid; s < ns; s += 256) {
-            const float ms = mbase[s * mstride];
-            l += ms == kNegInf ? 0.f : mbase[s * mstride + 1] * exp2f(ms - M);
-        }
-    l = wave_sum(l);
-    if (lane == 0) wred[wv] = l;
-    __syncthreads();
-    const float Ltot = wred[0] + wred[1] + wred[2] + wred[3];
-    const int dl = tid & 15, sl = tid >> 4;
-    const int dv = blockIdx.z * 16 + dl;
-    float acc = 0.f;
-    if (M != kNegInf) {
-        int s = sl;
-        for (; s + 48 < ns; s += 64) {
-            const float m0 = mbase[s * mstride], m1 = mbase[(s + 16) * mstride];
-            const float m2 = mbase[(s + 32) * mstride], m3 = mbase[(s + 48) * mstride];
-            const float o0 = obase[s * ostride + dv], o1 = obase[(s + 16) * ostride + dv];
-            const float o2 = obase[(s + 32) * ostride + dv], o3 = obase[(s + 48) * ostride + dv];
-            acc += (m0 == kNegInf ? 0.f : o0 * exp2f(m0 - M)) + (m1 == kNegInf ? 0.f : o1 * exp2f(m1 - M)) +
-                   (m2 == kNegInf ? 0.f : o2 * exp2f(m2 - M)) + (m3 == kNegInf ? 0.f : o3 * exp2f(m3 - M));
-        }
-        for (; s < ns; s += 16) {
-            const float ms = mbase[s * mstride];
-            if (ms != kNegInf) acc += obase[s * ostride + dv] * exp2f(ms - M);
-        }
-    }
-    red[sl][dl] = acc;
-    __syncthreads();
-    if (tid < 16) {
-        float tot = 0.f;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) tot += red[q][tid];
-        const int dvo = blockIdx.z * 16 + tid;
-        cr.o[((int64_t)r * H + h) * D + dvo] = Ltot > 0.f ? tot / Ltot : 0.f;
-        if (dvo == 0 && cr.lse) cr.lse[(int64_t)r * H + h] = Ltot > 0.f ? M + log2f(Ltot) : kNegInf;
-    }
+    __shared__ CombineWideLds S;
+    combine_wide_body<D>(a, blockIdx.x, blockIdx.y, blockIdx.z, S);
 }
 
-// Few splits: one workgroup per (row, head), one thread per dv.  Splits are merged in batches of 16 whose
-// loads are all in flight together, with the running maximum rescaled between batches; the
-// (m, l) loads of a batch are the same for every thread of the workgroup.
+// Few splits: one workgroup per (row, head), one thread per dv.
 template <int D>
 __global__ __launch_bounds__(D) void attn_split_combine_kernel(AttnArgs a) {
-    constexpr int BATCH = 16;
-    const CombineRow cr = combine_row(a);
-    const int r = cr.r, h = blockIdx.y, H = a.H, ns = a.nsplit;
-    const int dv = threadIdx.x;
-    const float* obase = cr.part + ((int64_t)r * ns * H + h) * D + dv;     // split s at + s * H * D
-    const float* mbase = cr.part_ml + ((int64_t)r * ns * H + h) * 2;      // split s at + s * H * 2
-    float M = kNegInf, L = 0.f, acc = 0.f;
-    for (int s0 = 0; s0 < ns; s0 += BATCH) {
-        float2 ml[BATCH];
-        float ov[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int sp = s0 + u < ns ? s0 + u : ns - 1;
-            ml[u] = *(const float2*)(mbase + (int64_t)sp * H * 2);
-            ov[u] = obase[(int64_t)sp * H * D];
-        }
-        float mb = kNegInf;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) if (s0 + u < ns) mb = fmaxf(mb, ml[u].x);
-        const float Mn = fmaxf(M, mb);
-        if (Mn == kNegInf) continue;                 // nothing seen yet
-        const float c = M == kNegInf ? 0.f : exp2f(M - Mn);
-        L *= c;
-        acc *= c;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            if (s0 + u < ns && ml[u].x != kNegInf) {
-                const float wgt = exp2f(ml[u].x - Mn);
-                L += ml[u].y * wgt;
-                acc += ov[u] * wgt;
-            }
-        }
-        M = Mn;
-    }
-    cr.o[((int64_t)r * H + h) * D + dv] = L > 0.f ? acc / L : 0.f;
-    if (dv == 0 && cr.lse) cr.lse[(int64_t)r * H + h] = L > 0.f ? M + log2f(L) : kNegInf;
+    combine_narrow_body<D>(a, blockIdx.x, blockIdx.y);
 }
 
 // ---- launcher ------------------------------------------------------------------------------------

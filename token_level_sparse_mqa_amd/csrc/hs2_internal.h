@@ -94,6 +94,14 @@ struct BridgeFp8Args {
     int64_t stride;
 };
 
+// The decode hybrid block in one launch: full layer, split merge, scores, selection, sparse layers.
+struct DecodeBlockArgs {
+    AttnArgs full;
+    ScoreArgs score;
+    SelectArgs sel;
+    AttnArgs sparse;
+};
+
 // Kernel launchers (return the launch status).
 hipError_t launch_attn_generic(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t s);
@@ -104,6 +112,7 @@ hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s);
 bool bridge_rows_fits(const BridgeArgs& a);
 hipError_t launch_bridge_rows(const BridgeArgs& a, hipStream_t s);
 hipError_t launch_bridge_fp8(const BridgeFp8Args& a, hipStream_t s);
+hipError_t launch_decode_block(const DecodeBlockArgs& a, hipStream_t s);
 hipError_t launch_attn_rows_mfma(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_attn_split_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_rows_mfma(const ScoreArgs& a, hipStream_t s);

@@ -1,114 +1,8 @@
-// Token-level top-k selection with a forced recent window.
-//
-// Per query row at position t (kucoin news flash; lynxflow blog, "Token-Level Sparse
-// Selection"): the k_global best candidates j in [0, t - window] by (score desc, index asc),
-// written ascending, then -1 padding; followed by the window max(0, t-window+1)..t and -1
-// padding.  Scores are sums of probabilities, hence >= 0, so their binary32 bit patterns
-// order like the values and an exact radix select over the 32 bits finds the k-th largest
-// score T.  Everything above T is picked; among scores equal to T the lowest indices are
-// picked.  All decisions are taken on the bit patterns: integer work, bit-exact.
-//
-// Kernels (radix digits [31:21] [20:10] [9:0]):
-//   select_hist    per row segment: histogram of the top digit, summed into a row histogram
-//   select_gather  per row segment: entries whose top digit is above the k-th's are sure
-//                  picks; entries in the k-th's bucket become candidates (value, index)
-//   select_finish  per row: resolves the remaining digits and the ties among the candidates
-//                  in LDS, sorts the k picks ascending, writes the window and padding.  When
-//                  the k-th bucket holds more than kSelCap entries it falls back to exact
-//                  streaming passes over the row in global memory.
-#include "hs2_device.h"
+// Selection kernels.  Device code of the histogram digit search, the gather and the finish:
+// select_dev.h (shared with the single-launch decode block).
+#include "select_dev.h"
 
 namespace hs2 {
-
-__device__ __forceinline__ uint32_t dig1(uint32_t key) { return key >> 21; }
-__device__ __forceinline__ uint32_t dig2(uint32_t key) { return (key >> 10) & 0x7ffu; }
-__device__ __forceinline__ uint32_t dig3(uint32_t key) { return key & 0x3ffu; }
-
-// Given a histogram over NBINS digits (global or LDS memory) and a rank k, find the digit
-// holding the k-th largest entry and the number of entries with a larger digit.  Every wave
-// that calls it computes the same result on its own (no barrier): lane l sums the NBINS/64
-// digits NBINS-1-l*PER .. NBINS-(l+1)*PER, a shuffle scan over the lanes gives each lane the
-// count above its digits, and the lane that holds the k-th entry broadcasts it.  Should the
-// histogram hold fewer than k entries, digit 0 is reported (callers bound their writes).
-template <int NBINS>
-__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k, uint32_t& digit, uint32_t& above) {
-    constexpr int PER = NBINS / 64;
-    const int lane = threadIdx.x & 63;
-    const uint32_t* hb = hist + NBINS - (lane + 1) * PER;   // this lane's digits, ascending
-    uint32_t c[PER];
-#pragma unroll
-    for (int i = 0; i < PER; i += 4) {
-        const uint4 q = *(const uint4*)(hb + i);
-        c[i] = q.x; c[i + 1] = q.y; c[i + 2] = q.z; c[i + 3] = q.w;
-    }
-    uint32_t local = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) local += c[i];
-    uint32_t incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    const uint32_t total = __shfl(incl, 63);
-    uint32_t run = incl - local;        // entries with a digit above this lane's digits
-    int found = -1;
-    uint32_t fab = 0;
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {   // this lane's digits, descending
-        if (run < k && run + c[i] >= k) { found = NBINS - (lane + 1) * PER + i; fab = run; }
-        run += c[i];
-    }
-    const uint64_t m = __ballot(found >= 0);
-    if (m) {
-        const int src = __ffsll((unsigned long long)m) - 1;
-        digit = (uint32_t)__shfl(found, src);
-        above = __shfl(fab, src);
-    } else {
-        digit = 0;
-        above = total - __shfl(c[0], 63);    // lane 63 holds digits PER-1 .. 0
-    }
-}
-
-// Block-level digit search for a histogram in LDS: thread t reads consecutive digits (no bank
-// conflicts) and a block scan orders the threads.  Same result convention as wave_find_digit;
-// every thread of the block calls it and receives the result.
-template <int NT>
-__device__ void block_find_digit(const uint32_t* hist, int nbins, uint32_t k, uint32_t& digit, uint32_t& above,
-                                 uint32_t* tmp, uint32_t* res) {
-    const int per = (nbins + NT - 1) / NT;
-    const int x0 = threadIdx.x * per;
-    uint32_t local = 0;
-    for (int x = x0; x < x0 + per && x < nbins; ++x) local += hist[nbins - 1 - x];
-    uint32_t total;
-    uint32_t run = block_excl_scan<NT>(local, tmp, &total);
-    for (int x = x0; x < x0 + per && x < nbins; ++x) {
-        const uint32_t c = hist[nbins - 1 - x];
-        const bool last = x == nbins - 1;
-        if ((run < k && run + c >= k) || (last && run + c < k)) { res[0] = (uint32_t)(nbins - 1 - x); res[1] = run; }
-        run += c;
-    }
-    __syncthreads();
-    digit = res[0];
-    above = res[1];
-}
-
-__device__ __forceinline__ void row_info(const SelectArgs& a, int r, int64_t* t, int64_t* C) {
-    *t = row_pos(a.q_pos, a.kv_len, r, a.Tq, a.Nmax);
-    *C = cand_count(*t, a.window);
-}
-
-// Wave-aggregated append: returns the slot of this lane (valid where `pred`).
-__device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
-    const uint64_t m = __ballot(pred);
-    if (!m) return 0;
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll((unsigned long long)m) - 1;
-    uint32_t base = 0;
-    if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, leader);
-    return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-}
 
 __global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
     __shared__ uint32_t hist[kHistBins];
@@ -128,275 +22,14 @@ __global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
         if (hist[x]) atomicAdd(&a.rowhist[(int64_t)r * kHistBins + x], hist[x]);
 }
 
-// Each workgroup counts its sure picks and bucket candidates, reserves space for them with one
-// atomic per counter, then writes them (per-row counters stay uncontended).
 __global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
-    constexpr int PER = kSelSeg / 256;
-    __shared__ uint32_t tmp[8];
-    __shared__ uint32_t basev[2];
-    const int r = blockIdx.x, seg = blockIdx.y;
-    int64_t t, C;
-    row_info(a, r, &t, &C);
-    if (C <= a.k_global) return;
-    const int64_t j0 = (int64_t)seg * kSelSeg;
-    if (j0 >= C) return;
-    const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
-    uint32_t b1, above1;
-    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)a.k_global, b1, above1);
-    const float* sc = a.scores + (int64_t)r * a.cstride;
-    uint32_t key[PER];
-    uint32_t ns = 0, nc = 0;
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int64_t j = j0 + u * 256 + threadIdx.x;
-        key[u] = j < j1 ? __float_as_uint(sc[j]) : 0u;
-        const uint32_t dg = dig1(key[u]);
-        ns += (j < j1 && dg > b1) ? 1u : 0u;
-        nc += (j < j1 && dg == b1) ? 1u : 0u;
-    }
-    uint32_t tot_s, tot_c;
-    uint32_t ps = block_excl_scan<256>(ns, tmp, &tot_s);
-    uint32_t pc = block_excl_scan<256>(nc, tmp, &tot_c);
-    uint32_t* cnt = a.counters + (int64_t)r * 4;
-    if (threadIdx.x == 0) {
-        basev[0] = tot_s ? atomicAdd(&cnt[0], tot_s) : 0u;
-        basev[1] = tot_c ? atomicAdd(&cnt[1], tot_c) : 0u;
-    }
-    __syncthreads();
-    ps += basev[0];
-    pc += basev[1];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int64_t j = j0 + u * 256 + threadIdx.x;
-        if (j >= j1) continue;
-        const uint32_t dg = dig1(key[u]);
-        if (dg > b1) {
-            // fewer than k_global entries lie above the k-th's bucket; the bound only matters
-            // if the row histogram disagreed with the scores
-            if (ps < (uint32_t)a.k_global) a.sure[(int64_t)r * a.k_global + ps] = (int32_t)j;
-            ++ps;
-        } else if (dg == b1) {
-            if (pc < (uint32_t)kSelCap) a.cand[(int64_t)r * kSelCap + pc] = make_uint2(key[u], (uint32_t)j);
-            ++pc;
-        }
-    }
-}
-
-constexpr int kFinThreads = 1024;
-
-// Ascending bitonic sort of n (power of two) 32-bit values in LDS.
-__device__ void bitonic_sort_i32(int32_t* v, int n) {
-    for (int k = 2; k <= n; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = threadIdx.x; i < n; i += kFinThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const int32_t x = v[i], y = v[ixj];
-                    const bool up = (i & k) == 0;
-                    if ((x > y) == up) { v[i] = y; v[ixj] = x; }
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// Writes the K <= kFinThreads distinct picks out[0..K) (values in [0, C)) to irow in ascending
-// order.  Each pick goes to bucket v >> sh (at most kRankBuckets buckets cover [0, C)); a scan
-// of the bucket counts gives each bucket's first output position, and a pick's rank within its
-// bucket is the number of smaller picks there (buckets span 2^sh indices, so they hold few
-// picks unless the picks cluster).  cnt and start hold kRankBuckets entries, items K.
-constexpr int kRankBuckets = 4096;
-
-__device__ void rank_sort_picks(const int32_t* out, int K, int64_t C, int32_t* irow, uint32_t* cnt,
-                                uint32_t* start, int32_t* items, uint32_t* tmp) {
-    int sh = 0;
-    while (((C - 1) >> sh) >= kRankBuckets) ++sh;
-    for (int x = threadIdx.x; x < kRankBuckets; x += kFinThreads) cnt[x] = 0;
-    __syncthreads();
-    const int t = threadIdx.x;
-    const int32_t v = t < K ? out[t] : -1;
-    const bool mine = v >= 0 && (int64_t)v < C;     // always, unless the counts disagreed
-    const int b = mine ? (int)((int64_t)v >> sh) : 0;
-    uint32_t slot = 0;
-    if (mine) slot = atomicAdd(&cnt[b], 1u);
-    __syncthreads();
-    constexpr int PER = kRankBuckets / kFinThreads;
-    uint32_t c[PER];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) { c[i] = cnt[PER * t + i]; sum += c[i]; }
-    uint32_t total;
-    uint32_t base = block_excl_scan<kFinThreads>(sum, tmp, &total);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) { start[PER * t + i] = base; base += c[i]; }
-    __syncthreads();
-    if (mine) items[start[b] + slot] = v;
-    __syncthreads();
-    if (mine) {
-        const uint32_t s0 = start[b], n = cnt[b];
-        uint32_t rank = s0;
-        for (uint32_t i = 0; i < n; ++i) rank += items[s0 + i] < v ? 1u : 0u;
-        irow[rank] = v;
-    }
+    __shared__ GatherLds S;
+    select_gather_body(a, blockIdx.x, blockIdx.y, S);
 }
 
 __global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
-    __shared__ uint32_t ckey[kSelCap];
-    __shared__ int32_t cidx[kSelCap];
-    __shared__ int32_t out[4096];
-    __shared__ uint32_t tmp[kFinThreads / 64 + 1];
-    __shared__ uint32_t res[2];
-    __shared__ uint32_t lcount[2];
-
-    const int r = blockIdx.x;
-    const int K = a.k_global, W = a.window;
-    int64_t t, C;
-    row_info(a, r, &t, &C);
-    int32_t* irow = a.idx + (int64_t)r * (K + W);
-    const float* sc = a.scores + (int64_t)r * a.cstride;
-
-    // window segment and the optional score dump
-    for (int w = threadIdx.x; w < W; w += kFinThreads) {
-        const int64_t j = t - W + 1 + w;
-        int32_t v = -1;
-        if (t >= 0) {
-            const int64_t first = t - W + 1 > 0 ? t - W + 1 : 0;
-            const int64_t jj = first + w;
-            v = jj <= t ? (int32_t)jj : -1;
-        }
-        (void)j;
-        irow[K + w] = v;
-    }
-    if (a.scores_dbg) {
-        float* dbg = a.scores_dbg + (int64_t)r * a.Nmax;
-        for (int64_t j = threadIdx.x; j < a.Nmax; j += kFinThreads) dbg[j] = j < C ? sc[j] : -1.0f;
-    }
-    if (C <= K) {
-        for (int j = threadIdx.x; j < K; j += kFinThreads) irow[j] = j < C ? j : -1;
-        return;
-    }
-
-    uint32_t b1, above1;
-    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)K, b1, above1);
-    const uint32_t k1 = (uint32_t)K - above1;
-    const uint32_t* cnt = a.counters + (int64_t)r * 4;
-    const uint32_t n_cand = cnt[1];
-    uint32_t b2, b3, above2, above3;
-
-    if (n_cand <= (uint32_t)kSelCap) {
-        // ---- fast path: the k-th bucket is in LDS ----
-        const uint2* cg = a.cand + (int64_t)r * kSelCap;
-        for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads) { const uint2 e = cg[x]; ckey[x] = e.x; cidx[x] = (int32_t)e.y; }
-        for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
-        __syncthreads();
-        for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads) atomicAdd(&hist[dig2(ckey[x])], 1u);
-        __syncthreads();
-        block_find_digit<kFinThreads>(hist, kHistBins, k1, b2, above2, tmp, res);
-        const uint32_t k2 = k1 - above2;
-        for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
-        __syncthreads();
-        for (uint32_t x = threadIdx.x; x < n_cand; x += kFinThreads)
-            if (dig2(ckey[x]) == b2) atomicAdd(&hist[dig3(ckey[x])], 1u);
-        __syncthreads();
-        block_find_digit<kFinThreads>(hist, 1024, k2, b3, above3, tmp, res);
-        const uint32_t need_eq = k2 - above3;          // ties at T still needed
-        const uint32_t n_eq = hist[b3];
-        const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
-        // sure picks from the gather pass
-        const uint32_t n_sure = above1 < (uint32_t)K ? above1 : (uint32_t)K;
-        for (uint32_t x = threadIdx.x; x < n_sure; x += kFinThreads) out[x] = a.sure[(int64_t)r * K + x];
-        if (threadIdx.x == 0) { lcount[0] = n_sure; lcount[1] = 0; }
-        // classify the bucket: above T -> picked; equal to T -> tie list (reusing ckey storage)
-        uint32_t myk[kSelCap / kFinThreads];
-        int32_t myi[kSelCap / kFinThreads];
-#pragma unroll
-        for (int u = 0; u < kSelCap / kFinThreads; ++u) {
-            const uint32_t x = threadIdx.x + u * kFinThreads;
-            myk[u] = x < n_cand ? ckey[x] : 0u;
-            myi[u] = x < n_cand ? cidx[x] : -1;
-        }
-        __syncthreads();
-        int32_t* ties = (int32_t*)ckey;
-#pragma unroll
-        for (int u = 0; u < kSelCap / kFinThreads; ++u) {
-            const uint32_t x = threadIdx.x + u * kFinThreads;
-            if (x < n_cand) {
-                if (myk[u] > T) {
-                    const uint32_t o = atomicAdd(&lcount[0], 1u);
-                    if (o < (uint32_t)K) out[o] = myi[u];
-                } else if (myk[u] == T) {
-                    ties[atomicAdd(&lcount[1], 1u)] = myi[u];   // at most n_cand <= kSelCap
-                }
-            }
-        }
-        __syncthreads();
-        const uint32_t base = lcount[0];
-        if (need_eq == n_eq) {
-            for (uint32_t x = threadIdx.x; x < n_eq; x += kFinThreads)
-                if (base + x < (uint32_t)K) out[base + x] = ties[x];
-        } else {
-            int np = 1;
-            while (np < (int)n_eq) np <<= 1;
-            for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= (int)n_eq) ties[x] = 0x7fffffff;
-            __syncthreads();
-            bitonic_sort_i32(ties, np);
-            for (uint32_t x = threadIdx.x; x < need_eq && x < n_eq; x += kFinThreads)
-                if (base + x < (uint32_t)K) out[base + x] = ties[x];
-        }
-        __syncthreads();
-        if (K <= kFinThreads) {
-            // the candidate and histogram arrays are free now
-            rank_sort_picks(out, K, C, irow, ckey, (uint32_t*)cidx, (int32_t*)hist, tmp);
-        } else {
-            int np = 1;
-            while (np < K) np <<= 1;
-            for (int x = threadIdx.x; x < np; x += kFinThreads) if (x >= K) out[x] = 0x7fffffff;
-            __syncthreads();
-            bitonic_sort_i32(out, np);
-            for (int x = threadIdx.x; x < K; x += kFinThreads) irow[x] = out[x];
-        }
-        return;
-    }
-
-    // ---- fallback: exact streaming passes over the row ----
-    for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
-    __syncthreads();
-    for (int64_t j = threadIdx.x; j < C; j += kFinThreads) {
-        const uint32_t key = __float_as_uint(sc[j]);
-        if (dig1(key) == b1) atomicAdd(&hist[dig2(key)], 1u);
-    }
-    __syncthreads();
-    block_find_digit<kFinThreads>(hist, kHistBins, k1, b2, above2, tmp, res);
-    const uint32_t k2 = k1 - above2;
-    const uint32_t pre = (b1 << 11) | b2;
-    for (int x = threadIdx.x; x < kHistBins; x += kFinThreads) hist[x] = 0;
-    __syncthreads();
-    for (int64_t j = threadIdx.x; j < C; j += kFinThreads) {
-        const uint32_t key = __float_as_uint(sc[j]);
-        if ((key >> 10) == pre) atomicAdd(&hist[dig3(key)], 1u);
-    }
-    __syncthreads();
-    block_find_digit<kFinThreads>(hist, 1024, k2, b3, above3, tmp, res);
-    const uint32_t need_eq = k2 - above3;
-    const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
-    // ordered pass: ties ranked by index with a running block scan
-    uint32_t run_eq = 0, run_out = 0;
-    for (int64_t jb = 0; jb < C; jb += kFinThreads) {
-        const int64_t j = jb + threadIdx.x;
-        uint32_t key = 0;
-        if (j < C) key = __float_as_uint(sc[j]);
-        const bool eq = j < C && key == T;
-        uint32_t tot_eq;
-        const uint32_t rank = run_eq + block_excl_scan<kFinThreads>(eq ? 1u : 0u, tmp, &tot_eq);
-        const bool pick = j < C && (key > T || (eq && rank < need_eq));
-        uint32_t tot_pick;
-        const uint32_t pos = run_out + block_excl_scan<kFinThreads>(pick ? 1u : 0u, tmp, &tot_pick);
-        if (pick && pos < (uint32_t)K) irow[pos] = (int32_t)j;
-        run_eq += tot_eq;
-        run_out += tot_pick;
-    }
+    __shared__ FinishLds<kFinThreads> S;
+    select_finish_body<kFinThreads>(a, blockIdx.x, S);
 }
 
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
