@@ -100,10 +100,10 @@ KERNEL_UNITS = {
     "decode_block": ("step", "hbm"),
 }
 KERNEL_SOURCES = {
-    "full_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
+    "full_attn_mfma": ["attn_rows.hip", "attn_rows_dev.h", "mfma_tiles.h"],
     "full_attn_prefill": ["attn_prefill.hip", "mfma_tiles.h"],
-    "sparse_attn_mfma": ["attn_rows.hip", "mfma_tiles.h"],
-    "sparse_attn_layers_mfma": ["attn_rows.hip", "mfma_tiles.h"],
+    "sparse_attn_mfma": ["attn_rows.hip", "attn_rows_dev.h", "mfma_tiles.h"],
+    "sparse_attn_layers_mfma": ["attn_rows.hip", "attn_rows_dev.h", "mfma_tiles.h"],
     "bridge_mfma": ["bridge_mfma.hip", "mfma_tiles.h"],
     "bridge_rows": ["bridge_rows.hip"],
     "bridge_fp8": ["bridge_fp8.hip"],
