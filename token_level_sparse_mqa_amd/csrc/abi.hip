@@ -168,16 +168,20 @@ ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
     for (size_t i = 0; i < g_prof.size(); ++i) if (g_prof[i].name == name) entry = (int)i;
     if (entry < 0) { g_prof.push_back(ProfEntry{name}); entry = (int)g_prof.size() - 1; }
     hipEvent_t a = get_event(), b = get_event();
-    if (!a || !b) return;
-    hipEventRecord(a, s);
-    g_pending.push_back(ProfPending{entry, a, b});
-    slot = (int)g_pending.size() - 1;
+    if (a && b && hipEventRecord(a, s) == hipSuccess) {
+        g_pending.push_back(ProfPending{entry, a, b});
+        slot = (int)g_pending.size() - 1;
+        return;
+    }
+    // no measurement for this launch (the launch itself is unaffected)
+    if (a) g_event_pool.push_back(a);
+    if (b) g_event_pool.push_back(b);
 }
 
 ProfScope::~ProfScope() {
     if (slot < 0) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
-    hipEventRecord(g_pending[slot].stop, stream);
+    if (hipEventRecord(g_pending[slot].stop, stream) != hipSuccess) g_pending[slot].entry = -1;
 }
 
 }  // namespace hs2
@@ -193,7 +197,11 @@ const char* hs2_version(void) { return "hs2 0.1.0 (gfx950)"; }
 void hs2_profile_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_prof_mu);
     if (enable) {
-        for (auto& p : g_pending) { hipEventSynchronize(p.stop); g_event_pool.push_back(p.start); g_event_pool.push_back(p.stop); }
+        for (auto& p : g_pending) {
+            if (p.entry >= 0) (void)hipEventSynchronize(p.stop);      // drain; the timings are discarded
+            g_event_pool.push_back(p.start);
+            g_event_pool.push_back(p.stop);
+        }
         g_pending.clear();
         g_prof.clear();
     }
@@ -204,8 +212,8 @@ int hs2_profile_read(int i, const char** name, double* total_ms, int64_t* launch
     std::lock_guard<std::mutex> lk(g_prof_mu);
     for (auto& p : g_pending) {
         float ms = 0.f;
-        hipEventSynchronize(p.stop);
-        if (hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
+        if (p.entry >= 0 && hipEventSynchronize(p.stop) == hipSuccess &&
+            hipEventElapsedTime(&ms, p.start, p.stop) == hipSuccess) {
             g_prof[p.entry].ms += ms;
             g_prof[p.entry].launches += 1;
         }
