@@ -43,13 +43,18 @@
  *    q_pos: [B, Tq] int32 absolute positions; kv_len: [B] int32 valid cache rows;
  *    o: [B, Tq, H, d] fp32; idx: [B, Tq, k_global + window] int32.
  *  - Supported: d in {64, 128}; 1 <= H <= 32; (q, kv) dtypes (F32, F32), (BF16, BF16) and
- *    (BF16, FP8_E4M3).  Other combinations return HS2_ERR_UNSUPPORTED.
+ *    (BF16, FP8_E4M3).  Other combinations return HS2_ERR_UNSUPPORTED.  The calls that select
+ *    (hs2_full_attn_select, hs2_full_attn_select_blocks, hs2_decode_block) take
+ *    Nmax <= HS2_MAX_SELECT_NMAX (65535 selection segments of 4096 keys); larger values return
+ *    HS2_ERR_UNSUPPORTED and their workspace-size queries return 0.
  *  - BF16/FP8 paths run on MFMA with fp32 accumulation.  Q.K^T uses the exact bf16 values
  *    (FP8 codes convert to bf16 exactly).  For P.V, calls with Tq < 8 query tokens per
  *    sequence (decode) and hs2_sparse_attn split the attention weights into a bf16 high and
  *    low part against bf16 V (weights kept to about 2^-16 relative); calls with Tq >= 8
  *    (query chunks) use fp16 weights against V converted to fp16, which is exact for bf16 V
- *    with |v| <= 65504 (larger values saturate).  fp32 paths compute in fp32 throughout.
+ *    with |v| <= 65504 (larger values saturate).  Query chunks whose cache rows span more than
+ *    2^31 bytes per sequence (Nmax > 8M keys at d = 128 in bf16) run on the decode kernels
+ *    instead, one query row per workgroup.  fp32 paths compute in fp32 throughout.
  */
 #ifndef HS2_H
 #define HS2_H
@@ -58,6 +63,9 @@
 #include <stdint.h>
 
 #include <hip/hip_runtime_api.h>
+
+/* Largest cache length (rows per sequence) of the calls that select. */
+#define HS2_MAX_SELECT_NMAX ((int64_t)65535 * 4096)
 
 #ifdef __cplusplus
 extern "C" {

@@ -265,3 +265,32 @@ def test_decode_block_workspace_size():
     assert both >= full + 3 * 8 * 9 * 32 * 130 * 4
     assert hs2.hs2_decode_block_workspace_size(8, 8, 32, 128, 131072, 1024, 128, hs2.HS2_BF16, 3) == 0
     assert hs2.hs2_decode_block_workspace_size(8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16, 0) == 0
+
+
+def test_select_cache_length_limit():
+    """Calls that select take at most HS2_MAX_SELECT_NMAX rows per sequence (one selection grid row
+    per 4096-key segment): above it they refuse before launching anything, and their size
+    queries return 0."""
+    big = hs2.HS2_MAX_SELECT_NMAX
+    assert hs2.hs2_full_attn_select_workspace_size(1, 1, 32, 128, big, 1024, 128, hs2.HS2_BF16) > big * 4
+    assert hs2.hs2_full_attn_select_workspace_size(1, 1, 32, 128, big + 1, 1024, 128, hs2.HS2_BF16) == 0
+    assert hs2.hs2_decode_block_workspace_size(1, 1, 32, 128, big + 1, 1024, 128, hs2.HS2_BF16, 3) == 0
+    assert _fas(N=big + 1) == hs2.HS2_ERR_UNSUPPORTED
+    assert "selection supports" in hs2.hs2_last_error()
+    assert _db(N=big + 1) == hs2.HS2_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kvd,row_bytes", [(hs2.HS2_BF16, 256), (hs2.HS2_FP8_E4M3, 128)])
+def test_long_chunk_takes_row_kernels(kvd, row_bytes):
+    """Query chunks whose cache spans more than 2^31 bytes per sequence leave the chunk kernels
+    (32-bit offsets) for the row kernels, whose key splits show up in the workspace as partial
+    results: 8 rows x 128 splits x 32 heads x (d + 2) floats."""
+    fit = (1 << 31) // row_bytes                     # the largest cache the chunk kernels take
+    a = hs2.hs2_full_attn_select_workspace_size(1, 8, 32, 128, fit, 1024, 128, kvd)
+    b = hs2.hs2_full_attn_select_workspace_size(1, 8, 32, 128, fit + 128, 1024, 128, kvd)
+    scores_growth = 8 * 128 * 4
+    assert b - a >= scores_growth + 8 * 128 * 32 * 130 * 4
+    # decode rows take the row kernels at every length: no jump there
+    c = hs2.hs2_full_attn_select_workspace_size(1, 4, 32, 128, fit, 1024, 128, kvd)
+    e = hs2.hs2_full_attn_select_workspace_size(1, 4, 32, 128, fit + 128, 1024, 128, kvd)
+    assert 0 <= e - c < 1 << 20

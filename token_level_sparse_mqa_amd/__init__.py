@@ -23,6 +23,7 @@ import torch
 
 HS2_F32, HS2_BF16, HS2_FP8_E4M3 = 0, 1, 2
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
+HS2_MAX_SELECT_NMAX = 65535 * 4096      # cache rows per sequence of the calls that select (hs2.h)
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libhs2.so")
 _LIB: Optional[ctypes.CDLL] = None

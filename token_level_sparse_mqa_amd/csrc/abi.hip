@@ -43,6 +43,13 @@ enum Path { PATH_GENERIC = 0, PATH_MFMA_ROWS = 1, PATH_MFMA_PREFILL = 2 };
 // query tokens per sequence from which the chunk kernels (8 queries sharing each K/V tile)
 // replace the one-row-per-workgroup kernels
 constexpr int kPrefillMinTq = 8;
+// The chunk kernels address a sequence's cache rows with 32-bit byte offsets: they take the
+// chunk only when Nmax rows of K (or V) span at most 2^31 bytes (8M keys at d = 128 in bf16);
+// longer caches take the row kernels, whose offsets are 64-bit.
+bool chunk_offsets_fit(int64_t Nmax, int d, int kv_dtype) {
+    const int64_t row_bytes = (int64_t)d * (kv_dtype == HS2_FP8_E4M3 ? 1 : 2);
+    return Nmax * row_bytes <= ((int64_t)1 << 31);
+}
 
 struct SelectPlan {
     Path path;
@@ -69,7 +76,8 @@ void split_range(int64_t R, int64_t n, int64_t target_wg, int64_t min_chunk, int
 SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, int kv_dtype) {
     SelectPlan p{};
     p.R = (int64_t)B * Tq;
-    p.path = kv_dtype == HS2_F32 ? PATH_GENERIC : (Tq >= kPrefillMinTq ? PATH_MFMA_PREFILL : PATH_MFMA_ROWS);
+    p.path = kv_dtype == HS2_F32 ? PATH_GENERIC
+             : (Tq >= kPrefillMinTq && chunk_offsets_fit(Nmax, d, kv_dtype) ? PATH_MFMA_PREFILL : PATH_MFMA_ROWS);
     if (p.path == PATH_MFMA_PREFILL) {
         p.nsplit = 1; p.chunk = Nmax;
         p.score_nsplit = 1; p.score_chunk = Nmax;
@@ -138,6 +146,14 @@ hs2_status check_common(const void* q, int q_dtype, const void* k, const void* v
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
         return fail(HS2_ERR_INVALID_ARG, "q/k/v/o must be 16-byte aligned");
     if (!aligned(k_scale, 4) || !aligned(v_scale, 4)) return fail(HS2_ERR_INVALID_ARG, "k_scale/v_scale must be 4-byte aligned");
+    return HS2_OK;
+}
+
+// the selection kernels run one grid row per 4096-key segment of a row
+hs2_status check_select_nmax(int64_t Nmax) {
+    if (Nmax > HS2_MAX_SELECT_NMAX)
+        return fail(HS2_ERR_UNSUPPORTED, "Nmax=%lld: selection supports at most %lld rows per sequence", (long long)Nmax,
+                    (long long)HS2_MAX_SELECT_NMAX);
     return HS2_OK;
 }
 
@@ -282,7 +298,8 @@ hs2_status hs2_kv_bridge_fp8(const void* hidden, int64_t T, int32_t D, const voi
 size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
                                            int32_t k_global, int32_t window, hs2_dtype kv_dtype) {
     (void)window;
-    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 || k_global < 1 || k_global > 4096)
+    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 || Nmax > HS2_MAX_SELECT_NMAX ||
+        k_global < 1 || k_global > 4096)
         return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
     return plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype).total;
@@ -360,6 +377,7 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
                                 int32_t k_global, int32_t window, float sm_scale, float* o, int32_t* idx,
                                 float* scores_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st == HS2_OK) st = check_select_nmax(Nmax);
     if (st != HS2_OK) return st;
     if (k_global < 1 || k_global > 4096) return fail(HS2_ERR_INVALID_ARG, "k_global=%d outside [1, 4096]", k_global);
     if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
@@ -386,7 +404,7 @@ size_t hs2_full_attn_select_blocks_workspace_size(int32_t B, int32_t Tq, int32_t
     (void)window;
     if (block < 1 || block > 64 || (block & (block - 1)) || k_blocks < 1 || (int64_t)k_blocks * block > 4096)
         return 0;
-    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1) return 0;
+    if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 || Nmax > HS2_MAX_SELECT_NMAX) return 0;
     if ((Nmax + block - 1) / block > kBlkMaxCand) return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
     const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_blocks * block, kv_dtype);
@@ -401,6 +419,7 @@ hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype, const v
                                        float* scores_dbg, void* workspace, size_t workspace_bytes,
                                        hipStream_t stream) {
     hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st == HS2_OK) st = check_select_nmax(Nmax);
     if (st != HS2_OK) return st;
     if (block < 1 || block > 64 || (block & (block - 1)))
         return fail(HS2_ERR_INVALID_ARG, "block=%d must be a power of two in [1, 64]", block);
@@ -460,6 +479,7 @@ DecodeBlockPlan plan_decode_block(int B, int Tq, int H, int d, int64_t Nmax, int
 size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
                                        int32_t k_global, int32_t window, hs2_dtype kv_dtype, int32_t L) {
     if (B < 0 || Tq < 0 || Tq >= kPrefillMinTq || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 ||
+        Nmax > HS2_MAX_SELECT_NMAX ||
         k_global < 1 || k_global > 4096 || window < 0 || window > 4096 || L < 1 || L > kMaxLayers)
         return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
@@ -473,6 +493,7 @@ hs2_status hs2_decode_block(const void* q, const void* const* q_sparse, int32_t 
                             float sm_scale, float* o, int32_t* idx, float* const* o_sparse, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
     hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
+    if (st == HS2_OK) st = check_select_nmax(Nmax);
     if (st != HS2_OK) return st;
     if (q_dtype != HS2_BF16) return fail(HS2_ERR_UNSUPPORTED, "the single-launch block takes bf16 queries");
     if (Tq >= kPrefillMinTq) return fail(HS2_ERR_UNSUPPORTED, "Tq=%d: the single-launch block is for decode rows (Tq < %d)", Tq, kPrefillMinTq);

@@ -16,6 +16,7 @@ constexpr int kSelCap = 4096;
 constexpr int kHistBins = 2048;
 // Row segment handled by one select workgroup.
 constexpr int kSelSeg = 4096;
+static_assert(HS2_MAX_SELECT_NMAX == (int64_t)65535 * kSelSeg, "one selection segment per grid row, at most 65535");
 constexpr int kBlkMaxCand = 16384;   // candidate blocks per row of the block-level selection
 
 // One attention problem: R = B*Tq query rows, each over a key set given either as the causal
