@@ -22,7 +22,8 @@ __global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
         if (hist[x]) atomicAdd(&a.rowhist[(int64_t)r * kHistBins + x], hist[x]);
 }
 
-__global__ __launch_bounds__(256) void select_gather_kernel(SelectArgs a) {
+// seven waves per SIMD: long query chunks run tens of thousands of these workgroups
+__global__ __launch_bounds__(256, 7) void select_gather_kernel(SelectArgs a) {
     __shared__ GatherLds S;
     select_gather_body(a, blockIdx.x, blockIdx.y, S);
 }

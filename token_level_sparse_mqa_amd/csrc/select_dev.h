@@ -112,18 +112,20 @@ __device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
     return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
-// Each workgroup counts its sure picks and bucket candidates, reserves space for them with one
-// atomic per counter, then writes them (per-row counters stay uncontended).
+// One workgroup of 256 threads: row r, segment seg of kSelSeg positions.  The counts of sure
+// picks (high half) and bucket candidates (low half; at most 4096 each per workgroup) are packed
+// into one word: a wave scan of the lanes' words, then one thread adds the four wave totals and
+// reserves space in both row lists with a single 64-bit atomic (counter 0 in the low word,
+// counter 1 in the high word; one atomic per workgroup, since atomics on a row's counters
+// serialise).  The order of the entries in the lists is arbitrary; the finish sorts what it
+// keeps.
 struct GatherLds {
-    uint32_t tmp[8];
-    uint32_t basev[2];
+    uint32_t wtot[4];
+    uint32_t wbase[4][2];
 };
 
-// One workgroup of 256 threads: row r, segment seg of kSelSeg positions.
 __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, int seg, GatherLds& S) {
     constexpr int PER = kSelSeg / 256;
-    uint32_t (&tmp)[8] = S.tmp;
-    uint32_t (&basev)[2] = S.basev;
     int64_t t, C;
     row_info(a, r, &t, &C);
     if (C <= a.k_global) return;
@@ -143,17 +145,39 @@ __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, i
         ns += (j < j1 && dg > b1) ? 1u : 0u;
         nc += (j < j1 && dg == b1) ? 1u : 0u;
     }
-    uint32_t tot_s, tot_c;
-    uint32_t ps = block_excl_scan<256>(ns, tmp, &tot_s);
-    uint32_t pc = block_excl_scan<256>(nc, tmp, &tot_c);
-    uint32_t* cnt = a.counters + (int64_t)r * 4;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const uint32_t mine = (ns << 16) | nc;
+    uint32_t incl = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(incl, o);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) S.wtot[w] = incl;
+    __syncthreads();
     if (threadIdx.x == 0) {
-        basev[0] = tot_s ? atomicAdd(&cnt[0], tot_s) : 0u;
-        basev[1] = tot_c ? atomicAdd(&cnt[1], tot_c) : 0u;
+        uint32_t run = 0;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint32_t tw = S.wtot[x];
+            S.wbase[x][0] = run >> 16;
+            S.wbase[x][1] = run & 0xffffu;
+            run += tw;
+        }
+        unsigned long long old = 0;
+        if (run)
+            old = atomicAdd((unsigned long long*)(a.counters + (int64_t)r * 4),
+                            ((unsigned long long)(run & 0xffffu) << 32) | (run >> 16));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            S.wbase[x][0] += (uint32_t)old;
+            S.wbase[x][1] += (uint32_t)(old >> 32);
+        }
     }
     __syncthreads();
-    ps += basev[0];
-    pc += basev[1];
+    const uint32_t excl = incl - mine;
+    uint32_t ps = S.wbase[w][0] + (excl >> 16);
+    uint32_t pc = S.wbase[w][1] + (excl & 0xffffu);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int64_t j = j0 + u * 256 + threadIdx.x;
