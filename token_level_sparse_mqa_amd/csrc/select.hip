@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256, 7) void select_gather_kernel(SelectArgs a) {
     select_gather_body(a, blockIdx.x, blockIdx.y, S);
 }
 
-__global__ __launch_bounds__(kFinThreads) void select_finish_kernel(SelectArgs a) {
+// eight waves per SIMD: two workgroups per CU (LDS allows two) for the many rows of query chunks
+__global__ __launch_bounds__(kFinThreads, 8) void select_finish_kernel(SelectArgs a) {
     __shared__ FinishLds<kFinThreads> S;
     select_finish_body<kFinThreads>(a, blockIdx.x, S);
 }

@@ -305,17 +305,28 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
         return;
     }
 
+    // every candidate slot the fast path may use is loaded before the digit search, so these
+    // loads, the candidate count and the histogram reads are in flight together (slots past the
+    // count hold stale values that are never used)
+    constexpr int CU = kSelCap / NT;
+    const uint2* cg = a.cand + (int64_t)r * kSelCap;
+    uint2 cpre[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) cpre[u] = cg[threadIdx.x + u * NT];
+    const uint32_t* cnt = a.counters + (int64_t)r * 4;
+    const uint32_t n_cand = cnt[1];
     uint32_t b1, above1;
     wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)K, b1, above1);
     const uint32_t k1 = (uint32_t)K - above1;
-    const uint32_t* cnt = a.counters + (int64_t)r * 4;
-    const uint32_t n_cand = cnt[1];
     uint32_t b2, b3, above2, above3;
 
     if (n_cand <= (uint32_t)kSelCap) {
         // ---- fast path: the k-th bucket is in LDS ----
-        const uint2* cg = a.cand + (int64_t)r * kSelCap;
-        for (uint32_t x = threadIdx.x; x < n_cand; x += NT) { const uint2 e = cg[x]; ckey[x] = e.x; cidx[x] = (int32_t)e.y; }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+            const uint32_t x = threadIdx.x + u * NT;
+            if (x < n_cand) { ckey[x] = cpre[u].x; cidx[x] = (int32_t)cpre[u].y; }
+        }
         for (int x = threadIdx.x; x < kHistBins; x += NT) hist[x] = 0;
         __syncthreads();
         for (uint32_t x = threadIdx.x; x < n_cand; x += NT) atomicAdd(&hist[dig2(ckey[x])], 1u);
