@@ -52,8 +52,8 @@
  *    sequence (decode) and hs2_sparse_attn split the attention weights into a bf16 high and
  *    low part against bf16 V (weights kept to about 2^-16 relative); calls with Tq >= 8
  *    (query chunks) use fp16 weights against V converted to fp16, which is exact for bf16 V
- *    with |v| <= 65504 (larger values saturate).  Query chunks whose cache rows span more than
- *    2^31 bytes per sequence (Nmax > 8M keys at d = 128 in bf16) run on the decode kernels
+ *    with |v| <= 65504 (larger values saturate).  Query chunks whose cache rows span 2^31 bytes
+ *    or more per sequence (Nmax >= 8M keys at d = 128 in bf16) run on the decode kernels
  *    instead, one query row per workgroup.  fp32 paths compute in fp32 throughout.
  */
 #ifndef HS2_H

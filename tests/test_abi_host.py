@@ -285,7 +285,7 @@ def test_long_chunk_takes_row_kernels(kvd, row_bytes):
     """Query chunks whose cache spans more than 2^31 bytes per sequence leave the chunk kernels
     (32-bit offsets) for the row kernels, whose key splits show up in the workspace as partial
     results: 8 rows x 128 splits x 32 heads x (d + 2) floats."""
-    fit = (1 << 31) // row_bytes                     # the largest cache the chunk kernels take
+    fit = (1 << 31) // row_bytes - 1                 # the largest cache the chunk kernels take
     a = hs2.hs2_full_attn_select_workspace_size(1, 8, 32, 128, fit, 1024, 128, kvd)
     b = hs2.hs2_full_attn_select_workspace_size(1, 8, 32, 128, fit + 128, 1024, 128, kvd)
     scores_growth = 8 * 128 * 4

@@ -44,11 +44,11 @@ enum Path { PATH_GENERIC = 0, PATH_MFMA_ROWS = 1, PATH_MFMA_PREFILL = 2 };
 // replace the one-row-per-workgroup kernels
 constexpr int kPrefillMinTq = 8;
 // The chunk kernels address a sequence's cache rows with 32-bit byte offsets: they take the
-// chunk only when Nmax rows of K (or V) span at most 2^31 bytes (8M keys at d = 128 in bf16);
+// chunk only when Nmax rows of K (or V) span less than 2^31 bytes (8M keys at d = 128 in bf16);
 // longer caches take the row kernels, whose offsets are 64-bit.
 bool chunk_offsets_fit(int64_t Nmax, int d, int kv_dtype) {
     const int64_t row_bytes = (int64_t)d * (kv_dtype == HS2_FP8_E4M3 ? 1 : 2);
-    return Nmax * row_bytes <= ((int64_t)1 << 31);
+    return Nmax * row_bytes < ((int64_t)1 << 31);
 }
 
 struct SelectPlan {

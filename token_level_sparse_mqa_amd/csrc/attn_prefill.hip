@@ -32,7 +32,7 @@ struct PfGeom {
 
 // Per-thread part of the cooperative tile loads: load x of a thread reads 16-byte chunk c of tile
 // row R, at byte offset (k0 + R) * RB + 16 c from the sequence's first cache row.  Offsets are
-// 32-bit (the host plans these kernels only where Nmax * row bytes is at most 2^31).
+// 32-bit (the host keeps Nmax * row bytes below 2^31).
 template <int D, int KV, int NT>
 struct PfLoader {
     using G = RawGeom<D, KV>;
