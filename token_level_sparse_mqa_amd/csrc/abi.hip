@@ -57,7 +57,7 @@ struct SelectPlan {
     int nsplit; int64_t chunk;         // attention pass over keys
     int score_nsplit; int64_t score_chunk;
     int nseg;
-    size_t off_part, off_lse, off_scores, off_hist, off_cnt, off_sure, off_cand, total;
+    size_t off_part, off_lse, off_scores, off_hist, off_cnt, off_sure, off_cand, off_digits, total;
 };
 
 // Split a key range of n entries over workgroups: at least `min_chunk` entries each (a multiple
@@ -103,6 +103,7 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
     p.off_sure = off;   off = align_up(off + (size_t)p.R * k_global * 4);
     p.off_cand = off;   off = align_up(off + (size_t)p.R * kSelCap * 8);
     p.off_scores = off; off = align_up(off + (size_t)p.R * Nmax * 4);
+    p.off_digits = off; off = align_up(off + (size_t)p.R * 2 * 4);
     p.total = off;
     return p;
 }
@@ -360,6 +361,7 @@ SelectArgs select_args(const SelectPlan& p, char* ws, const int32_t* q_pos, cons
     se.k_global = k_global; se.window = window; se.scores = (float*)(ws + p.off_scores); se.cstride = Nmax;
     se.rowhist = (uint32_t*)(ws + p.off_hist); se.counters = (uint32_t*)(ws + p.off_cnt);
     se.sure = (int32_t*)(ws + p.off_sure); se.cand = (uint2*)(ws + p.off_cand); se.nseg = p.nseg;
+    se.digits = (uint32_t*)(ws + p.off_digits);
     se.idx = idx; se.scores_dbg = scores_dbg;
     return se;
 }

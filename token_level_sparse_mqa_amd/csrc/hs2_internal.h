@@ -16,6 +16,7 @@ constexpr int kSelCap = 4096;
 constexpr int kHistBins = 2048;
 // Row segment handled by one select workgroup.
 constexpr int kSelSeg = 4096;
+constexpr int kSelDigitRows = 64;     // rows from which a launch finds each row's digit once
 static_assert(HS2_MAX_SELECT_NMAX == (int64_t)65535 * kSelSeg, "one selection segment per grid row, at most 65535");
 constexpr int kBlkMaxCand = 16384;   // candidate blocks per row of the block-level selection
 
@@ -70,6 +71,7 @@ struct SelectArgs {
     uint32_t* counters;                  // [R, 4]: sure count, candidate count
     int32_t* sure;                       // [R, k_global]
     uint2* cand;                         // [R, kSelCap] (key bits, index)
+    uint32_t* digits;                    // [R, 2]: the k-th's top digit and the count above it
     int nseg;
     int32_t* idx;                        // [R, k_global + window]
     float* scores_dbg;                   // [R, Nmax] or nullptr

@@ -22,16 +22,33 @@ __global__ __launch_bounds__(256) void select_hist_kernel(SelectArgs a) {
         if (hist[x]) atomicAdd(&a.rowhist[(int64_t)r * kHistBins + x], hist[x]);
 }
 
+// One wave per row: the k-th's top digit and the count above it, for the gather and the finish
+// of launches with many rows (each of their waves would otherwise read the row histogram).
+__global__ __launch_bounds__(64) void select_digit_kernel(SelectArgs a) {
+    const int r = blockIdx.x;
+    int64_t t, C;
+    row_info(a, r, &t, &C);
+    if (C <= a.k_global) return;
+    uint32_t b1, above1;
+    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)a.k_global, b1, above1);
+    if (threadIdx.x == 0) {
+        a.digits[2 * (int64_t)r] = b1;
+        a.digits[2 * (int64_t)r + 1] = above1;
+    }
+}
+
 // seven waves per SIMD: long query chunks run tens of thousands of these workgroups
+template <bool GIVEN>
 __global__ __launch_bounds__(256, 7) void select_gather_kernel(SelectArgs a) {
     __shared__ GatherLds S;
-    select_gather_body(a, blockIdx.x, blockIdx.y, S);
+    select_gather_body<GIVEN>(a, blockIdx.x, blockIdx.y, S);
 }
 
 // eight waves per SIMD: two workgroups per CU (LDS allows two) for the many rows of query chunks
+template <bool GIVEN>
 __global__ __launch_bounds__(kFinThreads, 8) void select_finish_kernel(SelectArgs a) {
     __shared__ FinishLds<kFinThreads> S;
-    select_finish_body<kFinThreads>(a, blockIdx.x, S);
+    select_finish_body<kFinThreads, GIVEN>(a, blockIdx.x, S);
 }
 
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
@@ -42,14 +59,25 @@ hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // launches of many rows find each row's digit once; a few long rows (decode) search it in
+    // every workgroup instead of paying for one more launch
+    const bool given = a.digits && a.R >= kSelDigitRows;
+    if (given) {
+        ProfScope ps("select_digit", s);
+        select_digit_kernel<<<a.R, 64, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     {
         ProfScope ps("select_gather", s);
-        select_gather_kernel<<<grid, 256, 0, s>>>(a);
+        if (given) select_gather_kernel<true><<<grid, 256, 0, s>>>(a);
+        else select_gather_kernel<false><<<grid, 256, 0, s>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     ProfScope ps("select_finish", s);
-    select_finish_kernel<<<a.R, kFinThreads, 0, s>>>(a);
+    if (given) select_finish_kernel<true><<<a.R, kFinThreads, 0, s>>>(a);
+    else select_finish_kernel<false><<<a.R, kFinThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 

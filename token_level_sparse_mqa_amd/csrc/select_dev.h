@@ -124,6 +124,9 @@ struct GatherLds {
     uint32_t wbase[4][2];
 };
 
+// GIVEN: the row's digit comes from a.digits (written by select_digit_kernel) instead of a search
+// over the row histogram in every wave.
+template <bool GIVEN = false>
 __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, int seg, GatherLds& S) {
     constexpr int PER = kSelSeg / 256;
     int64_t t, C;
@@ -133,7 +136,8 @@ __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, i
     if (j0 >= C) return;
     const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
     uint32_t b1, above1;
-    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)a.k_global, b1, above1);
+    if constexpr (GIVEN) b1 = a.digits[2 * (int64_t)r];
+    else wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)a.k_global, b1, above1);
     const float* sc = a.scores + (int64_t)r * a.cstride;
     uint32_t key[PER];
     uint32_t ns = 0, nc = 0;
@@ -268,7 +272,7 @@ struct FinishLds {
 };
 
 // One workgroup of NT threads: row r.
-template <int NT>
+template <int NT, bool GIVEN = false>
 __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, FinishLds<NT>& S) {
     uint32_t (&hist)[kHistBins] = S.hist;
     uint32_t (&ckey)[kSelCap] = S.ckey;
@@ -316,7 +320,12 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
     const uint32_t* cnt = a.counters + (int64_t)r * 4;
     const uint32_t n_cand = cnt[1];
     uint32_t b1, above1;
-    wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)K, b1, above1);
+    if constexpr (GIVEN) {
+        b1 = a.digits[2 * (int64_t)r];
+        above1 = a.digits[2 * (int64_t)r + 1];
+    } else {
+        wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)K, b1, above1);
+    }
     const uint32_t k1 = (uint32_t)K - above1;
     uint32_t b2, b3, above2, above3;
 
