@@ -101,6 +101,10 @@ SMALL = [
     # 128 query rows: the sparse layer takes the several-tiles-in-flight kernel (FP8 and d=64)
     small_config("rows128_fp8", 219, B=2, N=2000, Tq=64, kv_dtype="fp8", n_sparse=1),
     small_config("rows128_d64", 220, B=2, N=1500, Tq=64, H=16, d=64, n_sparse=1),
+    # decode rows of many sequences (64 rows or more): the row kernels with key splits, each
+    # row's top digit found once by its own launch before the gather and finish
+    small_config("rows72_many_seqs", 221, B=24, N=2500, Tq=3, n_sparse=1),
+    small_config("rows66_fp8", 222, B=66, N=1800, Tq=1, kv_dtype="fp8", n_sparse=1),
 ]
 
 
