@@ -10,6 +10,8 @@
 //
 // Kernels (radix digits [31:21] [20:10] [9:0]):
 //   select_hist    per row segment: histogram of the top digit, summed into a row histogram
+//   select_digit   per row (launches of many rows): the k-th's top digit and the count above
+//                  it, found once instead of in every workgroup of the next two kernels
 //   select_gather  per row segment: entries whose top digit is above the k-th's are sure
 //                  picks; entries in the k-th's bucket become candidates (value, index)
 //   select_finish  per row: resolves the remaining digits and the ties among the candidates
