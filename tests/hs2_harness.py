@@ -50,7 +50,7 @@ def bits_from_dev(t: torch.Tensor) -> np.ndarray:
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-class GpuRun:
+class HipRun:
     """Device copies of a workload and the HIP path's outputs."""
 
     def __init__(self, wl: Workload, dev="cuda"):

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from tests.hs2_harness import BAND, GpuRun, OracleRun, _say, to_dev, tol_for
+from tests.hs2_harness import BAND, HipRun, OracleRun, _say, to_dev, tol_for
 from workloads import CONFIGS, make_workload, small_config
 
 pytestmark = pytest.mark.gpu
@@ -51,7 +51,7 @@ def run_block_parity(cfg, kb=16, block=64, rows=None, sparse=True):
     _say(f"[blocks] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} {cfg.q_dtype}/{cfg.kv_dtype} kb={kb} block={block}")
     import token_level_sparse_mqa_amd as hs2
     wl = make_workload(cfg)
-    g = GpuRun(wl)
+    g = HipRun(wl)
     if cfg.bridge_D:
         g.bridge()
     o, bidx, idx = hs2.hs2_full_attn_select_blocks(g.q, g.k, g.v, g.q_pos, g.kv_len, k_scale=g.k_scale,
@@ -116,7 +116,7 @@ def test_block_one_is_token_level(Tq):
     """block = 1, k_blocks = k reproduces hs2_full_attn_select (same scores, same selection)."""
     import token_level_sparse_mqa_amd as hs2
     cfg = small_config(f"blk_one_{Tq}", 256 + Tq, B=2, N=4000, Tq=Tq, n_sparse=1)
-    g = GpuRun(make_workload(cfg))
+    g = HipRun(make_workload(cfg))
     _, idx_tok, _ = g.full()
     o, bidx, idx = hs2.hs2_full_attn_select_blocks(g.q, g.k, g.v, g.q_pos, g.kv_len, k_blocks=1024, block=1,
                                                    window=cfg.window, sm_scale=g.sm)

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.hs2_harness import GpuRun, OracleRun, _say, check_indices, tol_for, to_dev
+from tests.hs2_harness import HipRun, OracleRun, _say, check_indices, tol_for, to_dev
 from workloads import CONFIGS, make_workload, small_config
 
 pytestmark = pytest.mark.gpu
@@ -46,8 +46,8 @@ CASES = [
 def test_decode_block_equals_separate_calls(cfg):
     import token_level_sparse_mqa_amd as hs2
     _say(f"[decode_block] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} {cfg.kv_dtype} L={cfg.n_sparse}")
-    g1 = GpuRun(make_workload(cfg))
-    g2 = GpuRun(make_workload(small_config(cfg.name + "_b", cfg.cfg_id + 1000, B=cfg.B, N=cfg.N, Tq=cfg.Tq,
+    g1 = HipRun(make_workload(cfg))
+    g2 = HipRun(make_workload(small_config(cfg.name + "_b", cfg.cfg_id + 1000, B=cfg.B, N=cfg.N, Tq=cfg.Tq,
                                            H=cfg.H, d=cfg.d, q_dtype=cfg.q_dtype, kv_dtype=cfg.kv_dtype,
                                            n_sparse=cfg.n_sparse, k_global=cfg.k_global, window=cfg.window)))
     ws = hs2.decode_block_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global, cfg.window,
@@ -67,7 +67,7 @@ def test_decode_block_oracle():
     import token_level_sparse_mqa_amd as hs2
     cfg = CASES[0]
     wl = make_workload(cfg)
-    g = GpuRun(wl)
+    g = HipRun(wl)
     o, idx, osp = _fused(g, cfg, None)
     torch.cuda.synchronize()
     o, idx = o.cpu().numpy(), idx.cpu().numpy()
@@ -87,7 +87,7 @@ def test_decode_block_oracle():
 def test_decode_block_rejects():
     import token_level_sparse_mqa_amd as hs2
     cfg = CASES[0]
-    g = GpuRun(make_workload(cfg))
+    g = HipRun(make_workload(cfg))
     with pytest.raises(hs2.HS2Error):          # query chunks take the separate calls
         q = torch.zeros((cfg.B, 8, cfg.H, cfg.d), dtype=torch.bfloat16, device="cuda")
         hs2.hs2_decode_block(q, [q], g.k, g.v, torch.zeros((cfg.B, 8), dtype=torch.int32, device="cuda"), g.kv_len)

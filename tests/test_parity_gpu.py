@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from tests.hs2_harness import (GpuRun, OracleRun, _say, bits_from_dev, check_bridge, check_indices,
+from tests.hs2_harness import (HipRun, OracleRun, _say, bits_from_dev, check_bridge, check_indices,
                                to_dev, tol_for)
 from workloads import CONFIGS, make_workload, small_config
 
@@ -24,7 +24,7 @@ def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=
     _say(f"[parity] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} H={cfg.H} d={cfg.d} "
          f"{cfg.q_dtype}/{cfg.kv_dtype} k={cfg.k_global} W={cfg.window}")
     wl = make_workload(cfg)
-    g = GpuRun(wl)
+    g = HipRun(wl)
     if cfg.bridge_D:
         g.bridge()
     o, idx, dbg = g.full(scores_dbg=check_scores)
@@ -116,7 +116,7 @@ def test_small(cfg):
 def test_deterministic_indices():
     cfg = SMALL[0]
     wl = make_workload(cfg)
-    g = GpuRun(wl)
+    g = HipRun(wl)
     _, idx1, _ = g.full()
     _, idx2, _ = g.full()
     torch.cuda.synchronize()
@@ -131,7 +131,7 @@ def test_sparse_workspace_reuse():
     small = small_config("ws_reuse_small", 231, B=1, N=2000, Tq=1, n_sparse=1)
     runs = []
     for cfg in (big, small):
-        g = GpuRun(make_workload(cfg))
+        g = HipRun(make_workload(cfg))
         _, idx, _ = g.full()
         runs.append((cfg, g, idx))
     cfg0, g0, _ = runs[0]
@@ -152,7 +152,7 @@ def test_sparse_layers_match_per_layer(kv, B, Tq):
     cfg = small_config(f"layers_{kv}_{B}x{Tq}", 232 + (kv == "fp8") + 2 * (Tq > 8), B=B, N=3000, Tq=Tq,
                        n_sparse=3, kv_dtype=kv)
     _say(f"[layers] {cfg.name}")
-    g = GpuRun(make_workload(cfg))
+    g = HipRun(make_workload(cfg))
     _, idx, _ = g.full()
     for ws_on in (True, False):
         refs = [g.sparse(layer, idx, workspace=ws_on) for layer in range(3)]
@@ -181,7 +181,7 @@ def test_invalid_positions_give_empty_rows():
     wl = make_workload(cfg)
     wl.q_pos[0, 0] = 1500       # == kv_len
     wl.q_pos[1, 1] = -5
-    g = GpuRun(wl)
+    g = HipRun(wl)
     o, idx, _ = g.full()
     torch.cuda.synchronize()
     o, idx = o.cpu().numpy(), idx.cpu().numpy()
