@@ -5,6 +5,8 @@
 
 #include "hs2_device.h"
 
+#include <type_traits>
+
 namespace hs2 {
 
 constexpr int kCombineNarrowMax = 32;  // splits up to which a (row, head) workgroup merges alone
@@ -73,15 +75,26 @@ __device__ __forceinline__ void combine_wide_body(const AttnArgs& a, int bx, int
     const int dv = bz * 16 + dl;
     float acc = 0.f;
     if (M != kNegInf) {
+        // batches of U splits per thread with all their loads in flight together (16, then 8),
+        // so a long row's merge takes one or two round trips instead of one per four splits
         int s = sl;
-        for (; s + 48 < ns; s += 64) {
-            const float m0 = mbase[s * mstride], m1 = mbase[(s + 16) * mstride];
-            const float m2 = mbase[(s + 32) * mstride], m3 = mbase[(s + 48) * mstride];
-            const float o0 = obase[s * ostride + dv], o1 = obase[(s + 16) * ostride + dv];
-            const float o2 = obase[(s + 32) * ostride + dv], o3 = obase[(s + 48) * ostride + dv];
-            acc += (m0 == kNegInf ? 0.f : o0 * exp2f(m0 - M)) + (m1 == kNegInf ? 0.f : o1 * exp2f(m1 - M)) +
-                   (m2 == kNegInf ? 0.f : o2 * exp2f(m2 - M)) + (m3 == kNegInf ? 0.f : o3 * exp2f(m3 - M));
-        }
+        auto batch = [&](auto u_c) {
+            constexpr int U = decltype(u_c)::value;
+            for (; s + 16 * (U - 1) < ns; s += 16 * U) {
+                float mu[U], ou[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    mu[u] = mbase[(s + 16 * u) * mstride];
+                    ou[u] = obase[(s + 16 * u) * ostride + dv];
+                }
+                float part = 0.f;
+#pragma unroll
+                for (int u = 0; u < U; ++u) part += mu[u] == kNegInf ? 0.f : ou[u] * exp2f(mu[u] - M);
+                acc += part;
+            }
+        };
+        batch(std::integral_constant<int, 16>{});
+        batch(std::integral_constant<int, 8>{});
         for (; s < ns; s += 16) {
             const float ms = mbase[s * mstride];
             if (ms != kNegInf) acc += obase[s * ostride + dv] * exp2f(ms - M);
