@@ -51,8 +51,9 @@
  *    (FP8 codes convert to bf16 exactly).  For P.V, calls with Tq < 8 query tokens per
  *    sequence (decode) and hs2_sparse_attn split the attention weights into a bf16 high and
  *    low part against bf16 V (weights kept to about 2^-16 relative); calls with Tq >= 8
- *    (query chunks) use fp16 weights against V converted to fp16, which is exact for bf16 V
- *    with |v| <= 65504 (larger values saturate).  Query chunks whose cache rows span 2^31 bytes
+ *    (query chunks) use fp16 weights against V converted to fp16 by truncation, which is exact
+ *    for bf16 V with |v| in [2^-17, 65504] and 0 (smaller magnitudes lose less than 2^-24, larger
+ *    ones clamp to 65504).  Query chunks whose cache rows span 2^31 bytes
  *    or more per sequence (Nmax >= 8M keys at d = 128 in bf16) run on the decode kernels
  *    instead, one query row per workgroup.  fp32 paths compute in fp32 throughout.
  */
@@ -133,7 +134,9 @@ hs2_status hs2_kv_bridge_fp8(const void* hidden, int64_t T, int32_t D,
 
 /*
  * Bytes of workspace hs2_full_attn_select needs for these sizes (0 on invalid sizes).
- * The same value is valid for every call with sizes no larger than these and the same dtype.
+ * The same value is valid for every call with sizes no larger than these (B, Tq, H, d, Nmax,
+ * k_global) and the same KV dtype, whichever kernels that call takes: a size queried for a
+ * query chunk also covers decode calls with fewer query tokens.
  */
 size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d,
                                            int64_t Nmax, int32_t k_global, int32_t window,
@@ -163,7 +166,8 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Bytes of workspace hs2_full_attn_select_blocks needs for these sizes (0 on invalid sizes).
+ * Bytes of workspace hs2_full_attn_select_blocks needs for these sizes (0 on invalid sizes);
+ * valid for every call with no larger sizes and the same KV dtype, as above.
  */
 size_t hs2_full_attn_select_blocks_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d,
                                                   int64_t Nmax, int32_t k_blocks, int32_t block,
@@ -200,7 +204,8 @@ hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype,
                                        hipStream_t stream);
 
 /*
- * Bytes of workspace hs2_decode_block needs for these sizes (0 on invalid sizes).
+ * Bytes of workspace hs2_decode_block needs for these sizes (0 on invalid sizes); valid for every
+ * call with no larger sizes (B, Tq, H, d, Nmax, k_global, window, L) and the same KV dtype.
  */
 size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
                                        int32_t k_global, int32_t window, hs2_dtype kv_dtype, int32_t L);
@@ -257,6 +262,7 @@ hs2_status hs2_sparse_attn(const void* q, hs2_dtype q_dtype,
  * Bytes of optional workspace that let hs2_sparse_attn split each row's index list over
  * several workgroups (used when there are few rows, e.g. decode).  With a NULL or smaller
  * workspace each row is handled by one workgroup; results are the same up to fp32 rounding.
+ * The value serves every call with no larger sizes (B, Tq, H, d, S).
  */
 size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S);
 

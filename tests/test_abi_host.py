@@ -280,17 +280,71 @@ def test_select_cache_length_limit():
     assert _db(N=big + 1) == hs2.HS2_ERR_UNSUPPORTED
 
 
+def _need(fn, **kw):
+    """The exact workspace a call plans, read from its HS2_ERR_WORKSPACE message (a one-byte
+    workspace is refused on the host, before anything is launched)."""
+    assert fn(wsb=1, **kw) == hs2.HS2_ERR_WORKSPACE
+    m = re.search(r"workspace of (\d+) bytes needed", hs2.hs2_last_error())
+    assert m, hs2.hs2_last_error()
+    return int(m.group(1))
+
+
 @pytest.mark.parametrize("kvd,row_bytes", [(hs2.HS2_BF16, 256), (hs2.HS2_FP8_E4M3, 128)])
 def test_long_chunk_takes_row_kernels(kvd, row_bytes):
     """Query chunks whose cache spans more than 2^31 bytes per sequence leave the chunk kernels
-    (32-bit offsets) for the row kernels, whose key splits show up in the workspace as partial
-    results: 8 rows x 128 splits x 32 heads x (d + 2) floats."""
+    (32-bit offsets) for the row kernels, whose key splits show up in the call's own workspace
+    plan as partial results: 8 rows x 128 splits x 32 heads x (d + 2) floats."""
     fit = (1 << 31) // row_bytes - 1                 # the largest cache the chunk kernels take
-    a = hs2.hs2_full_attn_select_workspace_size(1, 8, 32, 128, fit, 1024, 128, kvd)
-    b = hs2.hs2_full_attn_select_workspace_size(1, 8, 32, 128, fit + 128, 1024, 128, kvd)
+    ks = vs = FAKE if kvd == hs2.HS2_FP8_E4M3 else None
+    a = _need(_fas, Tq=8, N=fit, kvd=kvd, ks=ks, vs=vs)
+    b = _need(_fas, Tq=8, N=fit + 128, kvd=kvd, ks=ks, vs=vs)
     scores_growth = 8 * 128 * 4
     assert b - a >= scores_growth + 8 * 128 * 32 * 130 * 4
     # decode rows take the row kernels at every length: no jump there
-    c = hs2.hs2_full_attn_select_workspace_size(1, 4, 32, 128, fit, 1024, 128, kvd)
-    e = hs2.hs2_full_attn_select_workspace_size(1, 4, 32, 128, fit + 128, 1024, 128, kvd)
+    c = _need(_fas, Tq=4, N=fit, kvd=kvd, ks=ks, vs=vs)
+    e = _need(_fas, Tq=4, N=fit + 128, kvd=kvd, ks=ks, vs=vs)
     assert 0 <= e - c < 1 << 20
+
+
+@pytest.mark.parametrize("kvd", [hs2.HS2_BF16, hs2.HS2_FP8_E4M3])
+def test_chunk_size_covers_decode_calls(kvd):
+    """A size queried for a query chunk (chunk kernels, no split partials) also covers every decode
+    call with fewer query tokens (row kernels, split partials) at the same cache length."""
+    ks = vs = FAKE if kvd == hs2.HS2_FP8_E4M3 else None
+    for B in (1, 3):
+        size = hs2.hs2_full_attn_select_workspace_size(B, 8, 32, 128, 131072, 1024, 128, kvd)
+        for b in range(1, B + 1):
+            for tq in range(1, 9):
+                assert _need(_fas, B=b, Tq=tq, N=131072, kvd=kvd, ks=ks, vs=vs) <= size, (B, b, tq)
+
+
+def test_workspace_sizes_cover_smaller_calls():
+    """Property: for random sizes, the queried workspace is at least the exact plan of every call
+    with no larger sizes (B, Tq, H, d, Nmax, k, window, L) and the same KV dtype."""
+    import random
+    rng = random.Random(20261203)
+    for _ in range(150):
+        kvd = rng.choice([hs2.HS2_F32, hs2.HS2_BF16, hs2.HS2_FP8_E4M3])
+        qd = hs2.HS2_F32 if kvd == hs2.HS2_F32 else hs2.HS2_BF16
+        ks = vs = FAKE if kvd == hs2.HS2_FP8_E4M3 else None
+        B, Tq = rng.randint(1, 12), rng.randint(1, 40)
+        H, d = rng.randint(1, 32), rng.choice([64, 128])
+        N, kg, W = rng.randint(1, 300000), rng.randint(1, 4096), rng.randint(0, 512)
+        size = hs2.hs2_full_attn_select_workspace_size(B, Tq, H, d, N, kg, W, kvd)
+        bsz = hs2.hs2_full_attn_select_blocks_workspace_size(B, Tq, H, d, N, max(1, kg // 64), 64, W, kvd)
+        for _ in range(6):
+            b, tq, h = rng.randint(1, B), rng.randint(1, Tq), rng.randint(1, H)
+            dd = rng.choice([64, d]) if d == 128 else 64
+            n, k = rng.randint(1, N), rng.randint(1, kg)
+            assert _need(_fas, B=b, Tq=tq, H=h, d=dd, N=n, kg=k, W=W, qd=qd, kvd=kvd, ks=ks, vs=vs) <= size
+            if bsz:
+                kb = max(1, k // 64)
+                if kb <= max(1, kg // 64):
+                    assert _need(_fasb, B=b, Tq=tq, H=h, d=dd, N=n, kb=kb, W=W, qd=qd, kvd=kvd, ks=ks, vs=vs) <= bsz
+        if qd == hs2.HS2_BF16 and Tq < 8 and kg + W <= 1152:
+            L = rng.randint(1, 8)
+            dsz = hs2.hs2_decode_block_workspace_size(B, Tq, H, d, N, kg, W, kvd, L)
+            for _ in range(4):
+                b, tq, h, n = rng.randint(1, B), rng.randint(1, Tq), rng.randint(1, H), rng.randint(1, N)
+                k, l = rng.randint(1, kg), rng.randint(1, L)
+                assert _need(_db, L=l, B=b, Tq=tq, H=h, d=d, N=n, kg=k, W=W, kvd=kvd, ks=ks, vs=vs) <= dsz

@@ -114,6 +114,40 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+def _expect(t: Optional[torch.Tensor], name: str, shape, dtypes, device, optional: bool = False):
+    """The C ABI sees only pointers, so buffer sizes are checked here: shape, dtype and device of a
+    caller-supplied tensor must be what the call reads or writes."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+_KV_DTYPES = (torch.float32, torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
+
+
+def _check_select_inputs(q, k, v, q_pos, kv_len, k_scale, v_scale):
+    """Shapes shared by the calls of the full layer: q [B,Tq,H,d], k/v [B,Nmax,d], q_pos [B,Tq],
+    kv_len [B], scales [B,Nmax] (FP8 caches only)."""
+    if q.dim() != 4 or k.dim() != 3:
+        raise ValueError("q must be [B, Tq, H, d] and k, v [B, Nmax, d]")
+    B, Tq, H, d = q.shape
+    dev = q.device
+    _expect(q, "q", (B, Tq, H, d), (torch.float32, torch.bfloat16), dev)
+    _expect(k, "k", (B, k.shape[1], d), _KV_DTYPES, dev)
+    _expect(v, "v", tuple(k.shape), (k.dtype,), dev)
+    _expect(q_pos, "q_pos", (B, Tq), (torch.int32,), dev)
+    _expect(kv_len, "kv_len", (B,), (torch.int32,), dev)
+    _expect(k_scale, "k_scale", (B, k.shape[1]), (torch.float32,), dev, optional=True)
+    _expect(v_scale, "v_scale", (B, k.shape[1]), (torch.float32,), dev, optional=True)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -200,6 +234,7 @@ def hs2_full_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_po
                          idx: Optional[torch.Tensor] = None, scores_dbg: Optional[torch.Tensor] = None,
                          workspace: Optional[torch.Tensor] = None, stream=None):
     """Full-attention MQA layer + token-level selection.  Returns (o fp32 [B,Tq,H,d], idx int32 [B,Tq,k+W])."""
+    _check_select_inputs(q, k, v, q_pos, kv_len, k_scale, v_scale)
     B, Tq, H, d = q.shape
     Nmax = k.shape[1]
     kvd = dtype_code(k)
@@ -209,6 +244,11 @@ def hs2_full_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_po
         o = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
     if idx is None:
         idx = torch.empty((B, Tq, k_global + window), dtype=torch.int32, device=q.device)
+    _expect(o, "o", (B, Tq, H, d), (torch.float32,), q.device)
+    _expect(idx, "idx", (B, Tq, k_global + window), (torch.int32,), q.device)
+    _expect(scores_dbg, "scores_dbg", (B, Tq, Nmax), (torch.float32,), q.device, optional=True)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError("workspace must be on the device of q")
     if workspace is None:
         n = hs2_full_attn_select_workspace_size(B, Tq, H, d, Nmax, k_global, window, kvd)
         workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=q.device)
@@ -234,6 +274,7 @@ def hs2_full_attn_select_blocks(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
                                 stream=None):
     """Full-attention MQA layer + block-level selection.  Returns (o fp32 [B,Tq,H,d],
     block_idx int32 [B,Tq,k_blocks], idx int32 [B,Tq,k_blocks*block+window])."""
+    _check_select_inputs(q, k, v, q_pos, kv_len, k_scale, v_scale)
     B, Tq, H, d = q.shape
     Nmax = k.shape[1]
     kvd = dtype_code(k)
@@ -245,6 +286,12 @@ def hs2_full_attn_select_blocks(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
         block_idx = torch.empty((B, Tq, k_blocks), dtype=torch.int32, device=q.device)
     if idx is None:
         idx = torch.empty((B, Tq, k_blocks * block + window), dtype=torch.int32, device=q.device)
+    _expect(o, "o", (B, Tq, H, d), (torch.float32,), q.device)
+    _expect(block_idx, "block_idx", (B, Tq, k_blocks), (torch.int32,), q.device)
+    _expect(idx, "idx", (B, Tq, k_blocks * block + window), (torch.int32,), q.device)
+    _expect(scores_dbg, "scores_dbg", (B, Tq, Nmax), (torch.float32,), q.device, optional=True)
+    if workspace is not None and workspace.device != q.device:
+        raise ValueError("workspace must be on the device of q")
     if workspace is None:
         n = hs2_full_attn_select_blocks_workspace_size(B, Tq, H, d, Nmax, k_blocks, block, window, kvd)
         workspace = torch.empty((max(n, 1),), dtype=torch.uint8, device=q.device)
@@ -255,12 +302,32 @@ def hs2_full_attn_select_blocks(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     return o, block_idx, idx
 
 
+def _check_sparse_inputs(qs, k, v, idx, kv_len, k_scale, v_scale, workspace):
+    """q [B,Tq,H,d] per layer, k/v [B,Nmax,d], idx [B,Tq,S], kv_len [B] (optional), scales [B,Nmax]."""
+    q = qs[0]
+    if q.dim() != 4 or k.dim() != 3 or idx.dim() != 3:
+        raise ValueError("q must be [B, Tq, H, d], k and v [B, Nmax, d], idx [B, Tq, S]")
+    B, Tq, H, d = q.shape
+    dev = q.device
+    for x in qs:
+        _expect(x, "q", (B, Tq, H, d), (torch.float32, torch.bfloat16), dev)
+    _expect(k, "k", (B, k.shape[1], d), _KV_DTYPES, dev)
+    _expect(v, "v", tuple(k.shape), (k.dtype,), dev)
+    _expect(idx, "idx", (B, Tq, idx.shape[-1]), (torch.int32,), dev)
+    _expect(kv_len, "kv_len", (B,), (torch.int32,), dev, optional=True)
+    _expect(k_scale, "k_scale", (B, k.shape[1]), (torch.float32,), dev, optional=True)
+    _expect(v_scale, "v_scale", (B, k.shape[1]), (torch.float32,), dev, optional=True)
+    if workspace is not None and workspace.device != dev:
+        raise ValueError("workspace must be on the device of q")
+
+
 def hs2_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                     kv_len: Optional[torch.Tensor] = None, k_scale: Optional[torch.Tensor] = None,
                     v_scale: Optional[torch.Tensor] = None, sm_scale: Optional[float] = None,
                     o: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                     stream=None) -> torch.Tensor:
     """Sparse layer reusing the full layer's KV and indices.  Returns o fp32 [B,Tq,H,d]."""
+    _check_sparse_inputs([q], k, v, idx, kv_len, k_scale, v_scale, workspace)
     B, Tq, H, d = q.shape
     Nmax = k.shape[1]
     S = idx.shape[-1]
@@ -268,6 +335,7 @@ def hs2_sparse_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torc
         sm_scale = 1.0 / math.sqrt(d)
     if o is None:
         o = torch.empty((B, Tq, H, d), dtype=torch.float32, device=q.device)
+    _expect(o, "o", (B, Tq, H, d), (torch.float32,), q.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().hs2_sparse_attn(
         _ptr(q), dtype_code(q), _ptr(k), _ptr(v), dtype_code(k), _ptr(k_scale), _ptr(v_scale), _ptr(idx), S,
@@ -296,12 +364,17 @@ def hs2_sparse_attn_layers(qs, k: torch.Tensor, v: torch.Tensor, idx: torch.Tens
     for q in qs:
         if q.shape != qs[0].shape or q.dtype != qs[0].dtype:
             raise ValueError("all layers' queries must have the same shape and dtype")
+    _check_sparse_inputs(qs, k, v, idx, kv_len, k_scale, v_scale, workspace)
     Nmax = k.shape[1]
     S = idx.shape[-1]
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(d)
     if os is None:
         os = [torch.empty((B, Tq, H, d), dtype=torch.float32, device=qs[0].device) for _ in range(L)]
+    if len(os) != L:
+        raise ValueError("one output per layer")
+    for o in os:
+        _expect(o, "o", (B, Tq, H, d), (torch.float32,), qs[0].device)
     qa = (ctypes.c_void_p * L)(*[_ptr(q) for q in qs])
     oa = (ctypes.c_void_p * L)(*[_ptr(o) for o in os])
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -331,6 +404,7 @@ def hs2_decode_block(q: torch.Tensor, qs, k: torch.Tensor, v: torch.Tensor, q_po
                      stream=None):
     """The decode hybrid block (full layer + selection + every sparse layer) in one launch.
     Returns (o fp32 [B,Tq,H,d], idx int32 [B,Tq,k+W], [o of each sparse layer])."""
+    _check_select_inputs(q, k, v, q_pos, kv_len, k_scale, v_scale)
     B, Tq, H, d = q.shape
     L = len(qs)
     Nmax = k.shape[1]
@@ -348,6 +422,16 @@ def hs2_decode_block(q: torch.Tensor, qs, k: torch.Tensor, v: torch.Tensor, q_po
     for x in qs:
         if x.shape != q.shape or x.dtype != q.dtype:
             raise ValueError("every sparse layer's queries must have the full layer's shape and dtype")
+    if len(os) != L:
+        raise ValueError("one output per sparse layer")
+    _expect(o, "o", (B, Tq, H, d), (torch.float32,), q.device)
+    _expect(idx, "idx", (B, Tq, k_global + window), (torch.int32,), q.device)
+    for x in list(os):
+        _expect(x, "o_sparse", (B, Tq, H, d), (torch.float32,), q.device)
+    for x in qs:
+        _expect(x, "q_sparse", (B, Tq, H, d), (q.dtype,), q.device)
+    if workspace.device != q.device:
+        raise ValueError("workspace must be on the device of q")
     qa = (ctypes.c_void_p * L)(*[_ptr(x) for x in qs])
     oa = (ctypes.c_void_p * L)(*[_ptr(x) for x in os])
     _check(lib().hs2_decode_block(

@@ -124,6 +124,43 @@ size_t sparse_ws_bytes(int64_t R, int H, int d, int S, int q_dtype) {
     return ns > 1 ? (size_t)R * ns * H * (d + 2) * 4 : 0;
 }
 
+// split_range gives R' rows at most min(ceil(target / R'), ceil(n / min_chunk)) splits each, so
+// for every R' <= R and n' <= n the split records number at most
+// min(target + R - 1, R * ceil(n / min_chunk)) (0 when no call can split).  The size queries
+// use this bound so that one workspace serves every call with no larger sizes, whichever plan
+// such a call takes.
+int64_t split_records_bound(int64_t R, int64_t n, int64_t target, int64_t min_chunk) {
+    const int64_t ns_max = ceil_div(n, min_chunk);
+    if (R <= 0 || ns_max <= 1) return 0;
+    const int64_t a = target + R - 1, b = R * ns_max;
+    return a < b ? a : b;
+}
+
+// Workspace bytes of hs2_full_attn_select for every call with sizes no larger than these (same
+// KV dtype): the exact plan's later buffers (linear in R, H, Nmax, k_global) after the largest
+// split-partial buffer any smaller call can need.  Query chunks (Tq >= 8) plan no partials, but
+// a call with fewer query tokens takes the row kernels, which do.
+size_t select_ws_bound(int B, int Tq, int H, int d, int64_t Nmax, int k_global, int kv_dtype) {
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
+    const size_t rest = p.total - p.off_lse;
+    int64_t R_rows, target, min_chunk;
+    if (kv_dtype == HS2_F32) {
+        R_rows = p.R; target = 4096; min_chunk = 256;
+    } else {
+        const int64_t tq_rows = chunk_offsets_fit(Nmax, d, kv_dtype) ? (Tq < kPrefillMinTq ? Tq : kPrefillMinTq - 1) : Tq;
+        R_rows = (int64_t)B * tq_rows; target = 1024; min_chunk = kv_dtype == HS2_FP8_E4M3 ? 2048 : 512;
+    }
+    const size_t part = (size_t)split_records_bound(R_rows, Nmax, target, min_chunk) * H * (d + 2) * 4;
+    const size_t own = p.off_lse;
+    return align_up(part > own ? part : own) + rest;
+}
+
+// Sparse-layer partials for every call with no larger sizes (one layer).
+size_t sparse_ws_bound(int64_t R, int H, int d, int S) {
+    const int64_t a = split_records_bound(R, S, 2048, 64), b = split_records_bound(R, S, 256, 128);
+    return (size_t)(a > b ? a : b) * H * (d + 2) * 4;
+}
+
 // every kernel reads q/k/v rows, hidden states and weights in 16-byte vectors
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -303,7 +340,7 @@ size_t hs2_full_attn_select_workspace_size(int32_t B, int32_t Tq, int32_t H, int
         k_global < 1 || k_global > 4096)
         return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
-    return plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype).total;
+    return select_ws_bound(B, Tq, H, d, Nmax, k_global, kv_dtype);
 }
 
 namespace {
@@ -409,8 +446,8 @@ size_t hs2_full_attn_select_blocks_workspace_size(int32_t B, int32_t Tq, int32_t
     if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || Nmax < 1 || Nmax > HS2_MAX_SELECT_NMAX) return 0;
     if ((Nmax + block - 1) / block > kBlkMaxCand) return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
-    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_blocks * block, kv_dtype);
-    return p.total + block_ws_extra(p.R, Nmax, block);
+    return select_ws_bound(B, Tq, H, d, Nmax, k_blocks * block, kv_dtype) +
+           block_ws_extra((int64_t)B * Tq, Nmax, block);
 }
 
 hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype, const void* k, const void* v,
@@ -485,7 +522,10 @@ size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t
         k_global < 1 || k_global > 4096 || window < 0 || window > 4096 || L < 1 || L > kMaxLayers)
         return 0;
     if ((int64_t)B * Tq == 0) return kAlign;
-    return plan_decode_block(B, Tq, H, d, Nmax, k_global, window, kv_dtype, L).total;
+    // every smaller call's own plan fits: the selection bound, then L layers' sparse partials
+    const int64_t R = (int64_t)B * Tq;
+    return select_ws_bound(B, Tq, H, d, Nmax, k_global, kv_dtype) +
+           align_up((size_t)L * split_records_bound(R, (int64_t)k_global + window, 256, 128) * H * (d + 2) * 4);
 }
 
 hs2_status hs2_decode_block(const void* q, const void* const* q_sparse, int32_t L, hs2_dtype q_dtype,
@@ -554,10 +594,8 @@ hs2_status hs2_decode_block(const void* q, const void* const* q_sparse, int32_t 
 
 size_t hs2_sparse_attn_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int32_t S) {
     if (B < 0 || Tq < 0 || H < 1 || H > 32 || (d != 64 && d != 128) || S < 1 || S > 8192) return 0;
-    // the workspace is sized for the larger of the fp32 and bf16 plans
-    size_t n = sparse_ws_bytes((int64_t)B * Tq, H, d, S, HS2_F32);
-    const size_t n2 = sparse_ws_bytes((int64_t)B * Tq, H, d, S, HS2_BF16);
-    if (n2 > n) n = n2;
+    // the larger of the fp32 and bf16 plans of every call with no larger sizes
+    const size_t n = sparse_ws_bound((int64_t)B * Tq, H, d, S);
     return n ? n : kAlign;
 }
 
