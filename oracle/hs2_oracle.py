@@ -225,23 +225,6 @@ def full_attn_select_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, t: int, sm
     return o, assemble_indices(g, t, k_global, window), score
 
 
-def full_attn_select(q: np.ndarray, k: np.ndarray, v: np.ndarray, q_pos: np.ndarray, sm: float,
-                     k_global: int = K_GLOBAL, window: int = WINDOW, rows=None):
-    """q [B,Tq,H,d], k/v [B,N,d] (float64), q_pos [B,Tq].
-
-    rows: optional list of (b, i) to evaluate (sampling); default all.
-    Returns dict rows -> (o, idx, score).
-    """
-    B, Tq = q_pos.shape
-    if rows is None:
-        rows = [(b, i) for b in range(B) for i in range(Tq)]
-    out = {}
-    for (b, i) in rows:
-        out[(b, i)] = full_attn_select_row(q[b, i], k[b], v[b], int(q_pos[b, i]), sm,
-                                           k_global, window)
-    return out
-
-
 # ----------------------------------------------------------------------------------------------
 # Block-level selection (the first-generation variant the token-level one replaces)
 # ----------------------------------------------------------------------------------------------
@@ -299,12 +282,3 @@ def sparse_attention_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.nd
     e = np.exp(s - m)
     p = e / e.sum(axis=1, keepdims=True)
     return p @ v[sel]
-
-
-def sparse_attn(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray, sm: float,
-                rows=None) -> dict:
-    """q [B,Tq,H,d], k/v [B,N,d], idx [B,Tq,S] -> dict (b,i) -> o [H,d]."""
-    B, Tq = idx.shape[:2]
-    if rows is None:
-        rows = [(b, i) for b in range(B) for i in range(Tq)]
-    return {(b, i): sparse_attention_row(q[b, i], k[b], v[b], idx[b, i], sm) for (b, i) in rows}

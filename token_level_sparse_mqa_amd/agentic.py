@@ -1,8 +1,9 @@
 """One agent trace over a growing KV cache: the multi-turn loop of the hybrid block.
 
 The pages' agentic loop alternates a short decoded action with a long observation that is
-prefilled, and the context only grows (ainews page, "Agentic inference as the driving workload";
-"How it fits into an agentic stack": observations are appended to one long context buffer, and
+prefilled, and the context only grows (agentik-os article, "How HySparse2 shrinks agent KV and
+prefill": section 1 "Agentic inference as the driving workload" and its "How it fits into an agentic
+stack": observations are appended to one long context buffer, and
 the cross-decoder K/V come from the self-decoder through the KV bridge).  A session holds one
 sequence's bf16 K/V cache at a fixed capacity and appends spans of tokens to it.  Appending T
 tokens at positions p .. p+T-1 is three calls of the C ABI, in stream order:

@@ -110,9 +110,10 @@ __device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
-// fp16 LDS tile from raw V, rows at a stride of ST bytes.  bf16 -> fp16 is exact for |v| in
-// [2^-14, 65504]; smaller values keep an absolute error below 2^-25, larger ones saturate.  FP8
-// codes convert exactly.
+// fp16 LDS tile from raw V, rows at a stride of ST bytes.  The conversion truncates (round toward
+// zero).  A bf16 value has 8 significant bits, so it is exact in fp16 for |v| in [2^-17, 65504]
+// (down to the fp16 subnormal step 2^-24); smaller magnitudes lose less than 2^-24, larger ones
+// clamp to 65504.  FP8 E4M3 codes (magnitudes 2^-9 .. 448) convert exactly.
 template <int D, int KV, int NT, int ST>
 __device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds, int tid) {
     using G = RawGeom<D, KV>;

@@ -3,7 +3,7 @@
 // KV Bridging (lynxflow blog, "Two-Level KV Sharing"; ainews page, mechanism paragraph): the
 // cross-decoder full layer's K/V rows come from self-decoder hidden states through the layer's
 // own projections.  In the agentic loop a decoded action token appends one row at a time
-// (ainews page, "Agentic inference as the driving workload"), so the product is a
+// (agentik-os article, section 1 "Agentic inference as the driving workload"), so the product is a
 // vector-matrix product that must read the 2 * D * d bf16 weights once; the MFMA tile kernel
 // (256 rows per workgroup, all 2d columns in one workgroup) would run one workgroup for it.
 //

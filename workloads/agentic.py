@@ -2,8 +2,9 @@
 
 The pages build the hybrid block around agentic inference: each round the agent emits a short
 action, the environment answers with a long observation that has to be prefilled, and the one
-context keeps growing (ainews page, "Agentic inference as the driving workload"; the same page's
-"How it fits into an agentic stack": append every observation to one long context buffer).  The
+context keeps growing (agentik-os article, "How HySparse2 shrinks agent KV and prefill": section 1
+"Agentic inference as the driving workload", and the same article's "How it fits into an agentic
+stack": every observation is appended to one long context buffer).  The
 pages give no lengths; the configs below pick a short action of a few dozen tokens and an
 observation of one 4,096-token chunk, starting from a context that already holds a long trace.
 
