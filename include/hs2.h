@@ -68,6 +68,9 @@
 /* Largest cache length (rows per sequence) of the calls that select. */
 #define HS2_MAX_SELECT_NMAX ((int64_t)65535 * 4096)
 
+/* Bytes of the static per-GPU scratch that hs2_full_attn_select_noalloc works in (64 MiB). */
+#define HS2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -164,6 +167,31 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype,
                                 int32_t k_global, int32_t window, float sm_scale,
                                 float* o, int32_t* idx, float* scores_dbg,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * hs2_full_attn_select for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  It computes exactly what
+ * hs2_full_attn_select computes (same kernels, same results) but works in a static scratch array
+ * that the library holds on every GPU it runs on, HS2_NOALLOC_SCRATCH_BYTES bytes per GPU, from
+ * module load until the process ends.  It calls no hipMalloc, hipFree or other allocating routine.
+ *   Limit: the sizes must need at most HS2_NOALLOC_SCRATCH_BYTES of workspace
+ *   (hs2_full_attn_select_workspace_size); larger ones return HS2_ERR_WORKSPACE before anything is
+ *   enqueued (64 MiB covers decode batches up to 64 sequences at 131072 keys).
+ *   Every call on one GPU shares that GPU's scratch, whose contents persist between calls: calls
+ *   that may overlap on one GPU (different streams, or host threads without ordering) race and
+ *   give undefined results; calls ordered on one stream are safe.  The kernels clear what must
+ *   start at zero themselves.
+ *   The stream must belong to the current device (otherwise HS2_ERR_INVALID_ARG).  The first call
+ *   on a device looks up that device's copy of the scratch (a HIP runtime query, no allocation).
+ * Other arguments, layouts, requirements and errors as for hs2_full_attn_select.
+ */
+hs2_status hs2_full_attn_select_noalloc(const void* q, hs2_dtype q_dtype,
+                                        const void* k, const void* v, hs2_dtype kv_dtype,
+                                        const float* k_scale, const float* v_scale,
+                                        const int32_t* q_pos, const int32_t* kv_len,
+                                        int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                        int32_t k_global, int32_t window, float sm_scale,
+                                        float* o, int32_t* idx, float* scores_dbg, hipStream_t stream);
 
 /*
  * Bytes of workspace hs2_full_attn_select_blocks needs for these sizes (0 on invalid sizes);

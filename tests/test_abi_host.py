@@ -348,3 +348,38 @@ def test_workspace_sizes_cover_smaller_calls():
                 b, tq, h, n = rng.randint(1, B), rng.randint(1, Tq), rng.randint(1, H), rng.randint(1, N)
                 k, l = rng.randint(1, kg), rng.randint(1, L)
                 assert _need(_db, L=l, B=b, Tq=tq, H=h, d=d, N=n, kg=k, W=W, kvd=kvd, ks=ks, vs=vs) <= dsz
+
+
+def _fna(**kw):
+    a = dict(q=FAKE, qd=hs2.HS2_BF16, k=FAKE, v=FAKE, kvd=hs2.HS2_BF16, ks=None, vs=None, qp=FAKE, kl=FAKE,
+             B=1, Tq=1, H=32, d=128, N=4096, kg=1024, W=128, sm=0.088, o=FAKE, idx=FAKE, dbg=None, stream=None)
+    a.update(kw)
+    return hs2.lib().hs2_full_attn_select_noalloc(a["q"], a["qd"], a["k"], a["v"], a["kvd"], a["ks"], a["vs"],
+                                                  a["qp"], a["kl"], a["B"], a["Tq"], a["H"], a["d"], a["N"], a["kg"],
+                                                  a["W"], a["sm"], a["o"], a["idx"], a["dbg"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), hs2.HS2_ERR_UNSUPPORTED),
+    (dict(kg=0), hs2.HS2_ERR_INVALID_ARG),
+    (dict(idx=None), hs2.HS2_ERR_INVALID_ARG),
+    (dict(o=FAKE + 4), hs2.HS2_ERR_INVALID_ARG),
+    (dict(B=0), hs2.HS2_OK),
+    # more workspace than the static scratch holds: refused before anything is enqueued
+    (dict(B=256, N=131072), hs2.HS2_ERR_WORKSPACE),
+    (dict(B=1, Tq=4096, N=69632), hs2.HS2_ERR_WORKSPACE),
+])
+def test_noalloc_rejects(kw, status):
+    assert _fna(**kw) == status
+    if status == hs2.HS2_ERR_WORKSPACE:
+        assert "static scratch holds" in hs2.hs2_last_error()
+
+
+def test_noalloc_limit_is_the_workspace_size():
+    """The static scratch takes every call whose workspace size is within HS2_NOALLOC_SCRATCH_BYTES:
+    decode128k (8 x 131072 keys) and decode1m_fp8 fit; 64 sequences of 131072 keys fit too."""
+    cap = hs2.HS2_NOALLOC_SCRATCH_BYTES
+    assert cap == 64 << 20
+    for args in ((8, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16), (1, 1, 32, 128, 1 << 20, 1024, 128, hs2.HS2_FP8_E4M3),
+                 (64, 1, 32, 128, 131072, 1024, 128, hs2.HS2_BF16)):
+        assert 0 < hs2.hs2_full_attn_select_workspace_size(*args) <= cap

@@ -5,6 +5,7 @@ called through its C ABI (include/hs2.h) with ctypes.  torch provides device mem
 the current stream.  The functions carry the C names:
 
     hs2_kv_bridge, hs2_kv_bridge_fp8, hs2_full_attn_select, hs2_full_attn_select_workspace_size,
+    hs2_full_attn_select_noalloc,
     hs2_full_attn_select_blocks, hs2_full_attn_select_blocks_workspace_size,
     hs2_sparse_attn, hs2_sparse_attn_workspace_size, hs2_sparse_attn_layers,
     hs2_sparse_attn_layers_workspace_size, hs2_decode_block, hs2_decode_block_workspace_size,
@@ -37,6 +38,9 @@ _SIGS = {
     "hs2_full_attn_select": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
                                             _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
                                             _vp, _vp, _vp, _vp, _sz, _vp]),
+    "hs2_full_attn_select_noalloc": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
+                                                    _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
+                                                    _vp, _vp, _vp, _vp]),
     "hs2_full_attn_select_blocks_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i64, _i32, _i32, _i32,
                                                          ctypes.c_int]),
     "hs2_full_attn_select_blocks": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, ctypes.c_int, _vp, _vp, _vp, _vp,
@@ -256,6 +260,32 @@ def hs2_full_attn_select(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_po
         _ptr(q), dtype_code(q), _ptr(k), _ptr(v), kvd, _ptr(k_scale), _ptr(v_scale), _ptr(q_pos), _ptr(kv_len),
         B, Tq, H, d, Nmax, k_global, window, float(sm_scale), _ptr(o), _ptr(idx), _ptr(scores_dbg),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+    return o, idx
+
+
+HS2_NOALLOC_SCRATCH_BYTES = 64 << 20      # static per-GPU scratch of hs2_full_attn_select_noalloc (hs2.h)
+
+
+def hs2_full_attn_select_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_pos: torch.Tensor,
+                                 kv_len: torch.Tensor, o: torch.Tensor, idx: torch.Tensor,
+                                 k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                                 k_global: int = 1024, window: int = 128, sm_scale: Optional[float] = None,
+                                 scores_dbg: Optional[torch.Tensor] = None, stream=None):
+    """hs2_full_attn_select working in the library's static per-GPU scratch instead of a workspace:
+    nothing is allocated, so the caller passes the outputs o fp32 [B,Tq,H,d] and idx int32 [B,Tq,k+W].
+    Calls that may overlap on one GPU share that scratch and race.  Returns (o, idx)."""
+    _check_select_inputs(q, k, v, q_pos, kv_len, k_scale, v_scale)
+    B, Tq, H, d = q.shape
+    Nmax = k.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    _expect(o, "o", (B, Tq, H, d), (torch.float32,), q.device)
+    _expect(idx, "idx", (B, Tq, k_global + window), (torch.int32,), q.device)
+    _expect(scores_dbg, "scores_dbg", (B, Tq, Nmax), (torch.float32,), q.device, optional=True)
+    _check(lib().hs2_full_attn_select_noalloc(
+        _ptr(q), dtype_code(q), _ptr(k), _ptr(v), dtype_code(k), _ptr(k_scale), _ptr(v_scale), _ptr(q_pos),
+        _ptr(kv_len), B, Tq, H, d, Nmax, k_global, window, float(sm_scale), _ptr(o), _ptr(idx), _ptr(scores_dbg),
+        _stream(stream)))
     return o, idx
 
 

@@ -240,6 +240,46 @@ ProfScope::~ProfScope() {
 
 }  // namespace hs2
 
+// ---- the static scratch of hs2_full_attn_select_noalloc -------------------------------------------
+// One copy per GPU, held from module load until the process ends.  Host code never passes the
+// array's name to a kernel or a copy: in host code it is a host-side stand-in, not a device address.
+// The address of each device's copy comes from hipGetSymbolAddress with that device current.
+static __device__ __align__(256) unsigned char scratch[HS2_NOALLOC_SCRATCH_BYTES];
+
+namespace hs2 {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_addr[kMaxDevices];
+
+// This call's device (the stream's device must be the current one) and its copy of `scratch`,
+// looked up on the first call on that device.
+hs2_status device_scratch(hipStream_t stream, char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(HS2_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if (sdev != dev)
+            return fail(HS2_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(HS2_ERR_HIP, "hipGetSymbolAddress(scratch) returned a null address");
+        g_scratch_addr[dev] = (char*)p;
+    }
+    *out = g_scratch_addr[dev];
+    return HS2_OK;
+}
+}  // namespace
+}  // namespace hs2
+
 using namespace hs2;
 
 extern "C" {
@@ -410,11 +450,14 @@ size_t block_ws_extra(int64_t R, int64_t Nmax, int block) {
 
 }  // namespace
 
-hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
-                                const float* k_scale, const float* v_scale, const int32_t* q_pos,
-                                const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
-                                int32_t k_global, int32_t window, float sm_scale, float* o, int32_t* idx,
-                                float* scores_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Host validation shared by hs2_full_attn_select and its variant that allocates nothing.
+hs2_status check_full_attn_select(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                                  const float* k_scale, const float* v_scale, const int32_t* q_pos,
+                                  const int32_t* kv_len, int B, int Tq, int H, int d, int64_t Nmax, int k_global,
+                                  int window, float sm_scale, const float* o, const int32_t* idx,
+                                  const float* scores_dbg) {
     hs2_status st = check_common(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, B, Tq, H, d, Nmax, sm_scale, o);
     if (st == HS2_OK) st = check_select_nmax(Nmax);
     if (st != HS2_OK) return st;
@@ -422,19 +465,61 @@ hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k,
     if (window < 0 || window > 4096) return fail(HS2_ERR_INVALID_ARG, "window=%d outside [0, 4096]", window);
     if ((int64_t)B * Tq == 0) return HS2_OK;
     if (!q_pos || !kv_len || !idx) return fail(HS2_ERR_INVALID_ARG, "null q_pos/kv_len/idx pointer");
-    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(scores_dbg, 4) || !aligned(workspace, 16))
-        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx/scores_dbg must be 4-byte and the workspace 16-byte aligned");
-    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
-    if (!workspace || workspace_bytes < p.total)
-        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
-    char* ws = (char*)workspace;
-    st = full_layer(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax, window,
-                    sm_scale, o, ws, stream);
+    if (!aligned(q_pos, 4) || !aligned(kv_len, 4) || !aligned(idx, 4) || !aligned(scores_dbg, 4))
+        return fail(HS2_ERR_INVALID_ARG, "q_pos/kv_len/idx/scores_dbg must be 4-byte aligned");
+    return HS2_OK;
+}
+
+// The full layer and the token-level selection on a validated call, with the plan's workspace at ws.
+hs2_status run_full_attn_select(const SelectPlan& p, const void* q, int q_dtype, const void* k, const void* v,
+                                int kv_dtype, const float* k_scale, const float* v_scale, const int32_t* q_pos,
+                                const int32_t* kv_len, int B, int Tq, int H, int d, int64_t Nmax, int k_global,
+                                int window, float sm_scale, float* o, int32_t* idx, float* scores_dbg, char* ws,
+                                hipStream_t stream) {
+    hs2_status st = full_layer(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax,
+                               window, sm_scale, o, ws, stream);
     if (st != HS2_OK) return st;
     const SelectArgs se = select_args(p, ws, q_pos, kv_len, Tq, Nmax, k_global, window, idx, scores_dbg);
     hipError_t e = launch_select(se, /*hist_done=*/true, stream);
     if (e != hipSuccess) return hip_fail(e, "select launch");
     return HS2_OK;
+}
+
+}  // namespace
+
+hs2_status hs2_full_attn_select(const void* q, hs2_dtype q_dtype, const void* k, const void* v, hs2_dtype kv_dtype,
+                                const float* k_scale, const float* v_scale, const int32_t* q_pos,
+                                const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
+                                int32_t k_global, int32_t window, float sm_scale, float* o, int32_t* idx,
+                                float* scores_dbg, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    hs2_status st = check_full_attn_select(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d,
+                                           Nmax, k_global, window, sm_scale, o, idx, scores_dbg);
+    if (st != HS2_OK || (int64_t)B * Tq == 0) return st;
+    if (!aligned(workspace, 16)) return fail(HS2_ERR_INVALID_ARG, "the workspace must be 16-byte aligned");
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
+    if (!workspace || workspace_bytes < p.total)
+        return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", p.total, workspace ? workspace_bytes : (size_t)0);
+    return run_full_attn_select(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax,
+                                k_global, window, sm_scale, o, idx, scores_dbg, (char*)workspace, stream);
+}
+
+hs2_status hs2_full_attn_select_noalloc(const void* q, hs2_dtype q_dtype, const void* k, const void* v,
+                                        hs2_dtype kv_dtype, const float* k_scale, const float* v_scale,
+                                        const int32_t* q_pos, const int32_t* kv_len, int32_t B, int32_t Tq, int32_t H,
+                                        int32_t d, int64_t Nmax, int32_t k_global, int32_t window, float sm_scale,
+                                        float* o, int32_t* idx, float* scores_dbg, hipStream_t stream) {
+    hs2_status st = check_full_attn_select(q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d,
+                                           Nmax, k_global, window, sm_scale, o, idx, scores_dbg);
+    if (st != HS2_OK || (int64_t)B * Tq == 0) return st;
+    const SelectPlan p = plan_select(B, Tq, H, d, Nmax, k_global, kv_dtype);
+    if (p.total > (size_t)HS2_NOALLOC_SCRATCH_BYTES)
+        return fail(HS2_ERR_WORKSPACE, "these sizes need %zu bytes of scratch; the static scratch holds %zu "
+                    "(use hs2_full_attn_select with a workspace)", p.total, (size_t)HS2_NOALLOC_SCRATCH_BYTES);
+    char* ws = nullptr;
+    st = device_scratch(stream, &ws);
+    if (st != HS2_OK) return st;
+    return run_full_attn_select(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax,
+                                k_global, window, sm_scale, o, idx, scores_dbg, ws, stream);
 }
 
 size_t hs2_full_attn_select_blocks_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t d, int64_t Nmax,
