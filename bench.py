@@ -25,6 +25,7 @@ METRIC = "query tokens/s for select+sparse attn at 128K & 1M ctx; % HBM/MFMA roo
 HBM_PEAK_GBS = 8000.0
 BLOCK = 64                      # block-level selection: positions per block
 BF16_PEAK_TFLOPS = 2500.0
+SLEEP_CYCLES = 200000           # ~0.1 ms of GPU sleep queued ahead of a timed region
 
 
 def log(msg):
@@ -499,6 +500,9 @@ def gather_cold_sweep(reps=5):
             flush.fill_(r & 0xFF)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            # a short GPU sleep ahead of the start event keeps the device busy while the host
+            # enqueues the call, so the events bracket the kernels and not the host's launch latency
+            torch.cuda._sleep(SLEEP_CYCLES)
             e0.record()
             hs2.hs2_sparse_attn(q, k, v, idx, o=o, workspace=ws)
             e1.record()

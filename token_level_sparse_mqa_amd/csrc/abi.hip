@@ -113,9 +113,10 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
 // be bandwidth-sized get long chunks and few splits to merge (measured on cold 1152-row
 // gathers: 15% faster than planning for 1024 workgroups).  The plan depends on one layer's rows
 // only, so a multi-layer launch gives every layer the bytes a one-layer launch gives it.
+constexpr int64_t kSparseTargetGroups = 256;
 void sparse_plan(int64_t R, int S, int q_dtype, int* nsplit, int64_t* chunk) {
     if (q_dtype == HS2_F32) split_range(R, S, 2048, 64, 32, nsplit, chunk);
-    else split_range(R, S, 256, 128, 128, nsplit, chunk);
+    else split_range(R, S, kSparseTargetGroups, 128, 128, nsplit, chunk);
 }
 
 size_t sparse_ws_bytes(int64_t R, int H, int d, int S, int q_dtype) {
@@ -157,7 +158,7 @@ size_t select_ws_bound(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
 
 // Sparse-layer partials for every call with no larger sizes (one layer).
 size_t sparse_ws_bound(int64_t R, int H, int d, int S) {
-    const int64_t a = split_records_bound(R, S, 2048, 64), b = split_records_bound(R, S, 256, 128);
+    const int64_t a = split_records_bound(R, S, 2048, 64), b = split_records_bound(R, S, kSparseTargetGroups, 128);
     return (size_t)(a > b ? a : b) * H * (d + 2) * 4;
 }
 
@@ -610,7 +611,7 @@ size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t
     // every smaller call's own plan fits: the selection bound, then L layers' sparse partials
     const int64_t R = (int64_t)B * Tq;
     return select_ws_bound(B, Tq, H, d, Nmax, k_global, kv_dtype) +
-           align_up((size_t)L * split_records_bound(R, (int64_t)k_global + window, 256, 128) * H * (d + 2) * 4);
+           align_up((size_t)L * split_records_bound(R, (int64_t)k_global + window, kSparseTargetGroups, 128) * H * (d + 2) * 4);
 }
 
 hs2_status hs2_decode_block(const void* q, const void* const* q_sparse, int32_t L, hs2_dtype q_dtype,

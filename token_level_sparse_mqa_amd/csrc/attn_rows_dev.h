@@ -41,15 +41,20 @@ struct RowTile {
 // Issue the loads of one tile.  Every load is unconditional (rows are clamped into the valid
 // range and masked keys are zeroed where the data is used), so the compiler counts outstanding
 // loads exactly and keeps them in flight across the computation of the previous tile.
-// `ids` holds the workgroup's key ids in LDS (list mode); in range mode key = entry.
-template <int D, int KV>
+// LIST: `ids` holds the workgroup's key ids in LDS; otherwise (range mode) key = entry.
+// Cache policy, measured on MI355X: in range mode (the full layer) K is loaded normally and V
+// non-temporally, so V's lines do not displace K's from the memory-side cache before the score
+// pass reads K again (decode128k: attention 103.5 -> 87 us, score pass 53.8 -> 47 us); in list
+// mode (the sparse layers) both are gathered non-temporally (cold 1152-row gathers of 256
+// queries: 79 -> 49 us).
+template <int D, int KV, bool LIST>
 __device__ __forceinline__ void load_row_tile(RowTile<D, KV>& T, const AttnArgs& a, int64_t rowbase, int64_t L,
                                               int64_t e_lo, int64_t e_hi, int64_t tile_e, const int32_t* ids) {
     const int lane = threadIdx.x & 63;
     const int m = lane & 31;
     const int64_t e = tile_e + m;
     int64_t j;
-    if (ids) {
+    if (LIST) {
         const int64_t ec = e < e_hi ? e : e_hi - 1;
         j = ids[ec - e_lo];
         if (e >= e_hi || j < 0 || j >= L) j = -1;
@@ -58,10 +63,10 @@ __device__ __forceinline__ void load_row_tile(RowTile<D, KV>& T, const AttnArgs&
     }
     T.kid = (int32_t)j;
     // a masked key reads the last key of the range (range mode) or row 0 (list mode)
-    const int32_t jr = (int32_t)(j >= 0 ? j : (ids ? 0 : e_hi - 1));
+    const int32_t jr = (int32_t)(j >= 0 ? j : (LIST ? 0 : e_hi - 1));
     auto src = [&](int R) { return rowbase + __shfl(jr, R); };
-    load_raw_tile<D, KV>(T.k, a.k, src);
-    load_raw_tile<D, KV>(T.v, a.v, src);
+    load_raw_tile<D, KV, LIST>(T.k, a.k, src);
+    load_raw_tile<D, KV, true>(T.v, a.v, src);
     if (KV == HS2_FP8_E4M3) {
         T.ks = a.k_scale[rowbase + jr];
         T.vs = a.v_scale[rowbase + jr];
@@ -185,8 +190,9 @@ struct RowLds {
     float mlf[32][2];
 };
 
-// One workgroup's work: block row bx (row, or layer * R + row), key split `split`.
-template <int D, int KV>
+// One workgroup's work: block row bx (row, or layer * R + row), key split `split`.  LIST: the
+// keys are the index list a.list (sparse layers), otherwise the causal range (the full layer).
+template <int D, int KV, bool LIST>
 __device__ __forceinline__ void attn_rows_body(const AttnArgs& a, int bx, int split, RowLds<D>& S) {
     constexpr int NW = kRowWaves;
     constexpr int NT = NW * 64;
@@ -213,7 +219,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs& a, int bx, int sp
     const int H = a.H;
     const int64_t L = seq_len(a.kv_len, b, a.Nmax);
     int64_t e0 = (int64_t)split * a.chunk, e1;
-    if (a.list) {
+    if (LIST) {
         e1 = e0 + a.chunk < a.S ? e0 + a.chunk : a.S;
         if (e1 - e0 > kRowListMax) e1 = e0 + kRowListMax;   // the host never plans more
     } else {
@@ -226,19 +232,40 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs& a, int bx, int sp
         for (int x = threadIdx.x; x < kHistBins; x += NT) a.zero_hist[(int64_t)r * kHistBins + x] = 0;
         if (threadIdx.x < 4) a.zero_cnt[(int64_t)r * 4 + threadIdx.x] = 0;
     }
+    // Prologue: Q (heads padded to 32 with zeros) becomes an LDS tile, the Q^T operand of every
+    // MFMA step, and the workgroup's list entries go to LDS.  Every load of the prologue is issued
+    // before the first one is used, so it costs one memory round trip instead of one per loop pass.
+    constexpr int CPR = LdsTile<D>::CPR;
+    constexpr int QX = (32 * CPR + NT - 1) / NT;
+    constexpr int IX = LIST ? (kRowListMax + NT - 1) / NT : 0;
     const int32_t* ids = nullptr;
-    if (a.list) {
-        for (int64_t x = threadIdx.x; x < e1 - e0; x += NT) S.ids[x] = a.list[(int64_t)r * a.S + e0 + x];
-        ids = S.ids;
-    }
-    // Q (heads padded to 32 with zeros) as an LDS tile: the Q^T operand of every MFMA step
     {
         const u32x4_t* qp = (const u32x4_t*)((const uint16_t*)qsrc + (int64_t)r * H * D);
-        constexpr int CPR = LdsTile<D>::CPR;
-        for (int x = threadIdx.x; x < 32 * CPR; x += NT) {
-            const int h = x / CPR, c = x % CPR;
-            *(u32x4_t*)(S.q + LdsTile<D>::off(h, c)) = h < H ? qp[h * CPR + c] : u32x4_t{0, 0, 0, 0};
+        u32x4_t qv[QX];
+#pragma unroll
+        for (int x = 0; x < QX; ++x) {
+            const int f = threadIdx.x + x * NT, h = f / CPR, c = f % CPR;
+            qv[x] = u32x4_t{0, 0, 0, 0};
+            if (f < 32 * CPR && h < H) qv[x] = qp[h * CPR + c];
         }
+        int32_t iv[IX > 0 ? IX : 1];
+#pragma unroll
+        for (int x = 0; x < IX; ++x) {
+            const int64_t e = threadIdx.x + (int64_t)x * NT;
+            iv[x] = -1;
+            if (e < e1 - e0) iv[x] = a.list[(int64_t)r * a.S + e0 + e];
+        }
+#pragma unroll
+        for (int x = 0; x < QX; ++x) {
+            const int f = threadIdx.x + x * NT;
+            if (f < 32 * CPR) *(u32x4_t*)(S.q + LdsTile<D>::off(f / CPR, f % CPR)) = qv[x];
+        }
+#pragma unroll
+        for (int x = 0; x < IX; ++x) {
+            const int64_t e = threadIdx.x + (int64_t)x * NT;
+            if (e < e1 - e0) S.ids[e] = iv[x];
+        }
+        if (LIST) ids = S.ids;
     }
     __syncthreads();
     RowWaveLds<D>& W = S.wl[w];
@@ -255,10 +282,10 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs& a, int bx, int sp
     const int64_t ntw = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles of this wave
     if (ntw > 0) {
         auto tile_e = [&](int64_t it) { return e0 + 32 * (w + (int64_t)NW * it); };
-        load_row_tile<D, KV>(T, a, rowbase, L, e0, e1, tile_e(0), ids);
+        load_row_tile<D, KV, LIST>(T, a, rowbase, L, e0, e1, tile_e(0), ids);
         for (int64_t it = 0; it + 1 < ntw; ++it) {
             const uint32_t valid = stage_row_tile<D, KV>(T, W);
-            load_row_tile<D, KV>(T, a, rowbase, L, e0, e1, tile_e(it + 1), ids);
+            load_row_tile<D, KV, LIST>(T, a, rowbase, L, e0, e1, tile_e(it + 1), ids);
             wave_lds_fence();
             row_tile_step<D, KV>(W, valid, S.q, oacc, m_run, l_run, sl2);
             wave_lds_fence();

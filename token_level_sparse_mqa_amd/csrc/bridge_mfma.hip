@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
         const uint32_t hk = (uint32_t)kc * BK * 2;                 // bytes along a hidden row
         const uint32_t wk = (uint32_t)kc * BK * DD * 2;            // bytes down the weights
 #pragma unroll
-        for (int x = 0; x < G::HX; ++x) rh[st][x] = *(const u32x4_t*)(hbase + (hoffs[x] + hk));
+        for (int x = 0; x < G::HX; ++x) rh[st][x] = ld16<false>(hbase + (hoffs[x] + hk));
 #pragma unroll
         for (int x = 0; x < G::WX; ++x)
             rw[st][x] = *(const u32x4_t*)((const char*)(wisk[x] ? a.wk : a.wv) + (woffs[x] + wk));

@@ -59,7 +59,7 @@ __global__ __launch_bounds__(kDbThreads, 2) void decode_block_kernel(DecodeBlock
 
     // full layer: (row, key split) items; split 0 of a row clears its selection workspace
     for (int it = blockIdx.x; it < R * p.full.nsplit; it += G) {
-        attn_rows_body<D, KV>(p.full, it / p.full.nsplit, it % p.full.nsplit, S.rows);
+        attn_rows_body<D, KV, false>(p.full, it / p.full.nsplit, it % p.full.nsplit, S.rows);
         __syncthreads();
     }
     grid.sync();
@@ -87,7 +87,7 @@ __global__ __launch_bounds__(kDbThreads, 2) void decode_block_kernel(DecodeBlock
     // sparse layers: (layer * R + row, split) items over the selected rows, then their merge
     const int RL = R * p.sparse.nlayer;
     for (int it = blockIdx.x; it < RL * p.sparse.nsplit; it += G) {
-        attn_rows_body<D, KV>(p.sparse, it / p.sparse.nsplit, it % p.sparse.nsplit, S.rows);
+        attn_rows_body<D, KV, true>(p.sparse, it / p.sparse.nsplit, it % p.sparse.nsplit, S.rows);
         __syncthreads();
     }
     if (p.sparse.nsplit > 1) {

@@ -90,9 +90,16 @@ struct RawGeom {
     static constexpr int NI = kTileRows / RPI;  // load instructions per tile
 };
 
+// 16-byte load; NT = non-temporal (the line is not kept in the caches for reuse).
+template <bool NT>
+__device__ __forceinline__ u32x4_t ld16(const void* p) {
+    if constexpr (NT) return __builtin_nontemporal_load((const u32x4_t*)p);
+    else return *(const u32x4_t*)p;
+}
+
 // Issue the NI coalesced loads of a tile: lane l of instruction x reads chunk l % CPR of tile
 // row RPI*x + l / CPR, whose cache row index is src_row(tile row).
-template <int D, int KV, class RowFn>
+template <int D, int KV, bool NT, class RowFn>
 __device__ __forceinline__ void load_raw_tile(u32x4_t* raw, const void* base, RowFn src_row) {
     using G = RawGeom<D, KV>;
     const int lane = threadIdx.x & 63;
@@ -101,7 +108,7 @@ __device__ __forceinline__ void load_raw_tile(u32x4_t* raw, const void* base, Ro
     for (int x = 0; x < G::NI; ++x) {
         const int R = G::RPI * x + lane / G::CPR;
         const int64_t row = src_row(R);
-        raw[x] = *(const u32x4_t*)((const char*)base + row * G::RB + 16 * c);
+        raw[x] = ld16<NT>((const char*)base + row * G::RB + 16 * c);
     }
 }
 

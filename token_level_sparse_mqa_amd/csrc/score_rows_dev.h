@@ -98,7 +98,7 @@ __device__ __forceinline__ void score_rows_body(const ScoreArgs& a, int bx, int 
         const int64_t j = e0 + 32 * tl + n < e1 ? e0 + 32 * tl + n : e1 - 1;
         const char* p = kbase + j * RB;
 #pragma unroll
-        for (int x = 0; x < NL; ++x) kr[x] = *(const u32x4_t*)(p + LSTRIDE * x);
+        for (int x = 0; x < NL; ++x) kr[x] = ld16<false>(p + LSTRIDE * x);
         if (KV == HS2_FP8_E4M3) ks = ksbase[j];
     };
     auto kop = [&](const u32x4_t* kr, int s) -> bf16x8_t {
