@@ -102,6 +102,8 @@ KERNEL_UNITS = {
 }
 KERNEL_SOURCES = {
     "full_attn_mfma": ["attn_rows.hip", "attn_rows_dev.h", "mfma_tiles.h"],
+    "score_rows_mfma": ["score_rows.hip", "score_rows_dev.h", "mfma_tiles.h"],
+    "score_prefill": ["attn_prefill.hip", "mfma_tiles.h"],
     "full_attn_prefill": ["attn_prefill.hip", "mfma_tiles.h"],
     "sparse_attn_mfma": ["attn_rows.hip", "attn_rows_dev.h", "mfma_tiles.h"],
     "sparse_attn_layers_mfma": ["attn_rows.hip", "attn_rows_dev.h", "mfma_tiles.h"],
@@ -136,7 +138,67 @@ def stored_traffic(workload, kernel):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def run_gpu(cfg, steps, warmup, profile=True, select="token", decode_block=False):
+def timed_steps(step, nsteps):
+    """K steps back to back on the current stream, an event before each and one after the last:
+    (median ms per step, mean ms per step, wall seconds of the region).  A short GPU sleep queued
+    ahead of the first event keeps the host's launch latency out of the first step."""
+    import torch
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    torch.cuda._sleep(SLEEP_CYCLES)
+    for i in range(nsteps):
+        ev[i].record(stream)
+        step()
+    ev[nsteps].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(nsteps))
+    return per[len(per) // 2], ev[0].elapsed_time(ev[nsteps]) / nsteps, wall
+
+
+def cold_steps(step, nsteps, flush):
+    """Median ms of one step with the L2 and memory-side cache flushed before it (a 512 MiB buffer
+    written between steps, outside the events)."""
+    import torch
+    per = []
+    for r in range(nsteps):
+        flush.fill_(r & 0xFF)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(SLEEP_CYCLES)
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1))
+    per.sort()
+    return per[len(per) // 2]
+
+
+def stored_counters(workload, kernel):
+    """Compute-unit counters of the kernel from the committed rocprofv3 summary
+    (profiles/<kernel>_<workload>_counters.json: MFMA busy, VALU busy), or None when there is none
+    or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("src_sha") != kernel_source_hash(kernel):
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "valu_busy", "mfma_flops_frac") if k in rec}
+
+
+def run_gpu(cfg, steps, warmup, profile=True, select="token", decode_block=False, layers="sequential",
+            supplements=True):
+    """One hybrid block per step.  layers="sequential": the sparse layers as one hs2_sparse_attn
+    call each, in order, as a decoder runs them (layer l+1's queries come from layer l's output);
+    layers="fused": all sparse layers in one hs2_sparse_attn_layers call (their queries given
+    up front).  Supplements: the other layer mode and a cold-cache step time."""
     import torch
 
     import token_level_sparse_mqa_amd as hs2
@@ -160,6 +222,7 @@ def run_gpu(cfg, steps, warmup, profile=True, select="token", decode_block=False
     ws = torch.empty((nws,), dtype=torch.uint8, device=dev)
     bidx = torch.empty((cfg.B, cfg.Tq, kb), dtype=torch.int32, device=dev)
     sws = hs2.sparse_attn_layers_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, cfg.n_sparse, dev)
+    sws1 = hs2.sparse_attn_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, dev)
     o = torch.empty((cfg.B, cfg.Tq, cfg.H, cfg.d), dtype=torch.float32, device=dev)
     idx = torch.empty((cfg.B, cfg.Tq, cfg.S), dtype=torch.int32, device=dev)
     o_sp = [torch.empty_like(o) for _ in range(cfg.n_sparse)]
@@ -168,15 +231,9 @@ def run_gpu(cfg, steps, warmup, profile=True, select="token", decode_block=False
         dbws = hs2.decode_block_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global, cfg.window, kvd,
                                           cfg.n_sparse, dev)
 
-    def step():
+    def full():
         if cfg.bridge_D:
             hs2.hs2_kv_bridge(t["hidden"], t["wk"], t["wv"], k_out=t["k"][0], v_out=t["v"][0])
-        if decode_block:
-            # the whole block (full layer, selection, sparse layers) in one launch
-            hs2.hs2_decode_block(t["q"], t["qs"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
-                                 v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
-                                 o=o, idx=idx, os=o_sp, workspace=dbws)
-            return
         if blocks:
             hs2.hs2_full_attn_select_blocks(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
                                             v_scale=t["v_scale"], k_blocks=kb, block=BLOCK, window=cfg.window,
@@ -185,39 +242,53 @@ def run_gpu(cfg, steps, warmup, profile=True, select="token", decode_block=False
             hs2.hs2_full_attn_select(t["q"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
                                      v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
                                      o=o, idx=idx, workspace=ws)
-        # the sparse layers share the K/V cache and the indices: one call (one launch per kernel)
+
+    def step_sequential():
+        full()
+        for layer in range(cfg.n_sparse):
+            hs2.hs2_sparse_attn(t["qs"][layer], t["k"], t["v"], idx, kv_len=t["kv_len"], k_scale=t["k_scale"],
+                                v_scale=t["v_scale"], sm_scale=sm, o=o_sp[layer], workspace=sws1)
+
+    def step_fused():
+        full()
         hs2.hs2_sparse_attn_layers(t["qs"], t["k"], t["v"], idx, kv_len=t["kv_len"], k_scale=t["k_scale"],
                                    v_scale=t["v_scale"], sm_scale=sm, os=o_sp, workspace=sws)
 
+    def step_block():
+        # the whole block (full layer, selection, sparse layers) in one launch
+        hs2.hs2_decode_block(t["q"], t["qs"], t["k"], t["v"], t["q_pos"], t["kv_len"], k_scale=t["k_scale"],
+                             v_scale=t["v_scale"], k_global=cfg.k_global, window=cfg.window, sm_scale=sm,
+                             o=o, idx=idx, os=o_sp, workspace=dbws)
+
+    step = step_block if decode_block else (step_sequential if layers == "sequential" else step_fused)
     log(f"[bench] warmup {warmup}")
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
 
-    def timed(nsteps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        e0.record(stream)
-        for _ in range(nsteps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / nsteps, time.perf_counter() - w0
-
-    # the step time comes from a region without per-kernel events (an event record between two
-    # kernels serialises them); the per-kernel durations from a second region of the same length
     log(f"[bench] timing {steps} steps")
-    ms, wall = timed(steps)
+    ms, ms_mean, wall = timed_steps(step, steps)
+    res = {"ms_per_step": ms, "ms_mean": ms_mean, "wall_s": wall, "rows": R, "wl": wl, "layers": layers}
+    if supplements and not decode_block:
+        other = step_fused if layers == "sequential" else step_sequential
+        for _ in range(2):
+            other()
+        res["ms_other_layers"], _, _ = timed_steps(other, steps)
+        log(f"[bench] cold-cache steps")
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        res["ms_cold"] = cold_steps(step, steps, flush)
+        del flush
     kernels = {}
     if profile:
+        # per-kernel durations from a second region of the same length (an event record between
+        # two kernels of a step serialises them, so the step time above has none)
         log(f"[bench] per-kernel event timing, {steps} steps")
         hs2.profile_enable(True)
-        timed(steps)
+        timed_steps(step, steps)
         kernels = hs2.profile_read()
         hs2.profile_enable(False)
-    return {"ms_per_step": ms, "wall_s": wall, "rows": R, "kernels": kernels, "wl": wl}
+    res["kernels"] = kernels
+    return res
 
 
 def agentic_units(cfg):
@@ -518,6 +589,26 @@ def gather_cold_sweep(reps=5):
                      "1 GiB bf16 K+V cache (not the timed step)", "points": out}
 
 
+def host_info():
+    """CPU model (from /proc/cpuinfo) and numpy's BLAS library (threadpoolctl)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{p.get('internal_api')} {p.get('version')}" for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
+    except Exception:  # pragma: no cover
+        pass
+    return {"cpu_model": model, "blas": blas}
+
+
 def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0, select="token"):
     """The float64 oracle, as it stands, on a bounded sample of the same workload: whole query
     rows, each with the full layer, the selection and every sparse layer, including decoding
@@ -561,7 +652,7 @@ def cpu_baseline(cfg, wl, budget_s=30.0, min_s=10.0, select="token"):
         el = time.perf_counter() - t0
         if el > budget_s or el >= min_s:
             break
-    return {"value": done / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": done / el, "unit": "query tokens/s", "cores": cores, "kind": "oracle", **host_info(),
             "sample": f"{done} query rows of {cfg.name} ({passes} pass(es) over its {len(rows)} rows; each "
                       f"row: full layer + {'block' if select == 'blocks' else 'token'}-level selection + {cfg.n_sparse} sparse layers, incl. decoding the "
                       f"cache), {el:.1f} s"}
@@ -581,6 +672,15 @@ def main():
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-gather-sweep", action="store_true",
                     help="skip the cold-cache gather sweep reported with the decode workloads")
+    ap.add_argument("--fused-layers", action="store_true",
+                    help="time the step with all sparse layers in one hs2_sparse_attn_layers call (their "
+                         "queries given up front) instead of one call per layer")
+    ap.add_argument("--no-supplements", action="store_true",
+                    help="time only the step (no other layer mode, no cold-cache steps): profiling runs")
+    ap.add_argument("--gather-sweep-only", action="store_true",
+                    help="run only the cold-cache gather sweep and print it (profiling of the sparse kernel)")
+    ap.add_argument("--no-1m", action="store_true",
+                    help="decode128k: skip the nested decode1m_fp8 record")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration runs)")
     args = ap.parse_args()
@@ -599,6 +699,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.gather_sweep_only:
+        print(json.dumps({"gather_cold_sweep": gather_cold_sweep()}), flush=True)
+        return
     from workloads import AGENTIC, BRIDGE_FP8, CONFIGS
     if args.workload in AGENTIC:
         agentic_main(AGENTIC[args.workload], args)
@@ -607,12 +710,41 @@ def main():
         bridge_fp8_main(BRIDGE_FP8[args.workload], args)
         return
     cfg = CONFIGS[args.workload]
+    layers = "fused" if args.fused_layers else "sequential"
     res = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile, select=args.select,
-                  decode_block=args.decode_block)
+                  decode_block=args.decode_block, layers=layers, supplements=not args.no_supplements)
+    out = workload_record(cfg, res, args)
+    out = {"metric": METRIC, **out}
+    if cfg.name == "decode128k" and not args.no_1m and not args.decode_block and args.select == "token":
+        # the metric is quoted at 128K and 1M context: the 1M FP8 decode block in the same run
+        res1m = run_gpu(CONFIGS["decode1m_fp8"], args.steps, args.warmup, profile=not args.no_profile,
+                        layers=layers, supplements=not args.no_supplements)
+        rec = workload_record(CONFIGS["decode1m_fp8"], res1m, args)
+        out["decode1m_fp8"] = {k: rec[k] for k in ("value", "unit", "ms_per_step", "ms_per_step_mean",
+                                                   "ms_per_step_fused_layers", "ms_per_step_sequential_layers",
+                                                   "ms_per_step_cold", "dtype", "config", "roofline",
+                                                   "full_select_frac", "step_roofline_frac", "kernels") if k in rec}
+    if cfg.Tq == 1 and not args.no_gather_sweep and not args.no_profile:
+        log("[bench] cold-cache gather sweep")
+        out["gather_cold_sweep"] = gather_cold_sweep()
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(cfg, res["wl"], select=args.select)
+    print(json.dumps(out), flush=True)
+
+
+# kernels of the full layer with its selection (the step minus the sparse layers and the bridge)
+FULL_SELECT_KERNELS = ("full_attn_mfma", "full_attn_combine", "full_attn_prefill", "full_attn_generic",
+                       "score_rows_mfma", "score_prefill", "score_generic", "select_digit", "select_gather",
+                       "select_finish", "block_max", "block_select")
+
+
+def workload_record(cfg, res, args):
+    """The bench fields of one workload's run: value, step times, roofline of the dominant kernel,
+    the full layer's HBM fraction and per-kernel times."""
     ms = res["ms_per_step"]
     value = res["rows"] / (ms / 1e3)
     alg = algorithmic(cfg)
-
     kernels = {}
     for name, (tot, n) in res["kernels"].items():
         kernels[name] = {"avg_us": 1e3 * tot / max(n, 1), "launches": n}
@@ -631,10 +763,13 @@ def main():
             ach = alg[unit]["flops"] / avg_s / 1e12
             roof = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": BF16_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": ach / BF16_PEAK_TFLOPS, "traffic": traffic}
+        cnt = stored_counters(cfg.name, kname)
+        if cnt is not None:
+            roof["counters"] = cnt
     step_frac = {"hbm": alg["step"]["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBS,
                  "mfma": alg["step"]["flops"] / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS}
     out = {
-        "metric": METRIC, "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+        "value": value, "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": {"f32": "f32", "bf16": "bf16"}[cfg.q_dtype] +
         ("+fp8kv" if cfg.kv_dtype == "fp8" else ""), "data": "synthetic",
@@ -642,16 +777,25 @@ def main():
                    "kv_dtype": cfg.kv_dtype, "k_global": cfg.k_global, "window": cfg.window,
                    "sparse_layers": cfg.n_sparse, "bridge_D": cfg.bridge_D,
                    "selection": "token" if args.select == "token" else f"blocks of {BLOCK}",
-                   "launch": "one launch (hs2_decode_block)" if args.decode_block else "one launch per kernel"},
+                   "launch": "one launch (hs2_decode_block)" if args.decode_block else
+                   ("one launch per kernel; the sparse layers one call each, in order" if res["layers"] == "sequential"
+                    else "one launch per kernel; all sparse layers in one call")},
+        "ms_per_step_mean": res["ms_mean"],
         "roofline": roof, "step_roofline_frac": step_frac, "kernels": kernels,
     }
-    if cfg.Tq == 1 and not args.no_gather_sweep and not args.no_profile:
-        log("[bench] cold-cache gather sweep")
-        out["gather_cold_sweep"] = gather_cold_sweep()
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(cfg, res["wl"], select=args.select)
-    print(json.dumps(out), flush=True)
+    if "ms_other_layers" in res:
+        other = "ms_per_step_fused_layers" if res["layers"] == "sequential" else "ms_per_step_sequential_layers"
+        out[other] = res["ms_other_layers"]
+        out["ms_per_step_" + res["layers"] + "_layers"] = ms
+    if "ms_cold" in res:
+        out["ms_per_step_cold"] = res["ms_cold"]
+    # the full layer with its selection against its algorithmic bytes (K and V read once)
+    fs = [kernels[k]["avg_us"] * kernels[k]["launches"] for k in FULL_SELECT_KERNELS if k in kernels]
+    if fs and "full_attn_mfma" in kernels:
+        per_step_s = sum(fs) / kernels["full_attn_mfma"]["launches"] / 1e6
+        out["full_select_frac"] = {"hbm": alg["full_attn"]["bytes"] / per_step_s / 1e9 / HBM_PEAK_GBS,
+                                   "us": per_step_s * 1e6, "kernels": [k for k in FULL_SELECT_KERNELS if k in kernels]}
+    return out
 
 
 if __name__ == "__main__":
