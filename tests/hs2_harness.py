@@ -120,6 +120,14 @@ class OracleRun:
             self.v = oracle.decode(wl.v, cfg.kv_dtype, wl.v_scale)
         self.sm = 1.0 / math.sqrt(cfg.d)
 
+    def use_bridged_cache(self, k_bits: np.ndarray, v_bits: np.ndarray):
+        """Stage cascade (reading R13): once the HIP bridge output has been validated against the
+        oracle's bridge, the later stages of the oracle run on those same cache bytes, so a
+        one-ulp bridge difference is judged once, by the bridge check, and not again through
+        every score and output that reads the row."""
+        self.k = oracle.decode(k_bits, "bf16")[None]
+        self.v = oracle.decode(v_bits, "bf16")[None]
+
     def full_row(self, b: int, i: int):
         t = int(self.wl.q_pos[b, i])
         return oracle.full_attn_select_row(self.q[b, i], self.k[b], self.v[b], t, self.sm,
@@ -151,22 +159,45 @@ def check_indices(idx_gpu: np.ndarray, idx_o: np.ndarray, score_o: np.ndarray, t
     return {"mismatch": int(diff.size // 2), "n": n}
 
 
-def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0, max_frac=1e-3):
+def fp32_sum_mismatch_rate(h: np.ndarray, w: np.ndarray, exact_bits: np.ndarray) -> float:
+    """Fraction of elements whose bf16 rounding changes when the D products of h @ w are summed in
+    fp32 one at a time (each addition rounded) instead of exactly.  Any fp32 accumulation order
+    moves a sum by about sqrt(additions) * 2^-24 of its size, and the rounding changes where the
+    exact value lies that close to a bf16 rounding boundary (midway between two bf16 values), so
+    the rate is a property of the data and of fp32, not of one kernel."""
+    import oracle
+    h32, w32 = h.astype(np.float32), w.astype(np.float32)
+    acc = np.zeros((h.shape[0], w.shape[1]), np.float32)
+    for c in range(h.shape[1]):
+        acc = acc + h32[:, c:c + 1] * w32[c:c + 1]
+    return float(np.mean(oracle.f64_to_bf16_bits_rne(acc.astype(np.float64)) != exact_bits))
+
+
+def check_bridge(hidden, wk, wv, kb, vb, ko, vo, sample=4096, seed=0, rate_check=True):
     """GPU bridge output vs the oracle's: the bit patterns may differ only where fp32 summation
-    can move the sum across a bf16 rounding boundary.  Bound per element (sampled rows):
-    |gpu - exact| <= D * 2^-24 * sum_i |h_i w_i| + one bf16 ulp of the exact value."""
+    can move the sum across a bf16 rounding boundary.
+      * per element (sampled rows): |gpu - exact| <= D * 2^-24 * sum_i |h_i w_i| + one bf16 ulp;
+      * the mismatch fraction (over all rows) at most three times what a sequential fp32 sum gives
+        on the sampled rows (the model's rate is about 1-2e-4 at D = 2048, N(0,1) hidden states
+        and N(0, 0.02) weights; MFMA accumulation in 16-product steps measures 2.5e-4), plus the
+        statistical slack of ten elements."""
     import oracle
     D = hidden.shape[1]
     frac_k, frac_v = float(np.mean(kb != ko)), float(np.mean(vb != vo))
-    _say(f"[parity] bridge mismatch fraction K {frac_k:.2e} V {frac_v:.2e}")
-    if max_frac is not None:      # a rate: meaningful over many elements only
-        assert frac_k < max_frac and frac_v < max_frac
     rows = np.random.default_rng(seed).choice(hidden.shape[0], size=min(sample, hidden.shape[0]), replace=False)
     h = oracle.decode(hidden[rows], "bf16")
-    for w_bits, got in ((wk, kb), (wv, vb)):
+    models = []
+    for w_bits, got, ref in ((wk, kb, ko), (wv, vb, vo)):
         w = oracle.decode(w_bits, "bf16")
         exact = h @ w
         mag = np.abs(h) @ np.abs(w)
         ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(exact), 2.0 ** -126))) - 7)
         err = np.abs(oracle.decode(got[rows], "bf16") - exact)
         assert np.all(err <= D * 2.0 ** -24 * mag + ulp)
+        if rate_check:
+            models.append(fp32_sum_mismatch_rate(h, w, ref[rows]))
+    _say(f"[parity] bridge mismatch fraction K {frac_k:.2e} V {frac_v:.2e}; sequential fp32 model "
+         f"{' '.join(f'{m:.2e}' for m in models)}")
+    if rate_check:
+        n = kb.size
+        assert frac_k <= 3 * models[0] + 10 / n and frac_v <= 3 * models[1] + 10 / n

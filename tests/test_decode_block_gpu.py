@@ -74,14 +74,27 @@ def test_decode_block_oracle():
     osp = [x.cpu().numpy() for x in osp]
     O = OracleRun(wl)
     tol = tol_for(cfg.kv_dtype)
+    idx_oracle = idx.copy()
     for b in range(cfg.B):
         for i in range(cfg.Tq):
             o_o, idx_o, sc_o = O.full_row(b, i)
             check_indices(idx[b, i], idx_o, sc_o, int(wl.q_pos[b, i]), cfg.k_global, cfg.window)
             assert np.max(np.abs(o[b, i] - o_o)) <= tol
-            if np.array_equal(idx[b, i], idx_o):
-                for l in range(cfg.n_sparse):
-                    assert np.max(np.abs(osp[l][b, i] - O.sparse_row(l, b, i, idx_o))) <= tol
+            idx_oracle[b, i] = idx_o
+            # the block's sparse layers on its own indices against the oracle on the same indices
+            for l in range(cfg.n_sparse):
+                assert np.max(np.abs(osp[l][b, i] - O.sparse_row(l, b, i, idx[b, i]))) <= tol
+    # and the sparse layers on the oracle's indices (rows whose selections differ inside the band
+    # included), through the same device code as the block's sparse phase
+    ws = hs2.sparse_attn_layers_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.S, cfg.n_sparse, g.q.device)
+    o_ref = hs2.hs2_sparse_attn_layers(g.qs, g.k, g.v, to_dev(idx_oracle, "i32"), kv_len=g.kv_len,
+                                       k_scale=g.k_scale, v_scale=g.v_scale, sm_scale=g.sm, workspace=ws)
+    torch.cuda.synchronize()
+    for l in range(cfg.n_sparse):
+        got = o_ref[l].cpu().numpy()
+        for b in range(cfg.B):
+            for i in range(cfg.Tq):
+                assert np.max(np.abs(got[b, i] - O.sparse_row(l, b, i, idx_oracle[b, i]))) <= tol
 
 
 def test_decode_block_rejects():

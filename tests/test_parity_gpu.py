@@ -21,6 +21,10 @@ pytestmark = pytest.mark.gpu
 
 
 def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=1e-7):
+    """The full layer, the selection and the sparse layers of one workload against the oracle on
+    the given rows (default: every row).  The sparse layers are checked both ways (reading R12):
+    the HIP path on the oracle's indices, and the HIP path on its own indices against the oracle
+    on those same indices."""
     _say(f"[parity] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} H={cfg.H} d={cfg.d} "
          f"{cfg.q_dtype}/{cfg.kv_dtype} k={cfg.k_global} W={cfg.window}")
     wl = make_workload(cfg)
@@ -29,11 +33,21 @@ def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=
         g.bridge()
     o, idx, dbg = g.full(scores_dbg=check_scores)
     torch.cuda.synchronize()
-    o_h, idx_h = o.cpu().numpy(), idx.cpu().numpy()
-    dbg_h = dbg.cpu().numpy() if dbg is not None else None
-    O = OracleRun(wl)
     if rows is None:
         rows = [(b, i) for b in range(cfg.B) for i in range(cfg.Tq)]
+    o_h, idx_h = o.cpu().numpy(), idx.cpu().numpy()
+    dbg_rows = None
+    if dbg is not None:       # only the checked rows come to the host (full chunks hold GBs of scores)
+        sel = torch.tensor([b * cfg.Tq + i for (b, i) in rows], dtype=torch.int64, device=dbg.device)
+        dbg_rows = dbg.view(cfg.B * cfg.Tq, cfg.N).index_select(0, sel).cpu().numpy()
+        del dbg
+    O = OracleRun(wl)
+    if cfg.bridge_D:
+        # the bridge stage first, against the oracle's float64 projection; the oracle's attention
+        # then reads the validated HIP cache (reading R13)
+        kb, vb = bits_from_dev(g.k[0]), bits_from_dev(g.v[0])
+        check_bridge(wl.hidden, wl.wk, wl.wv, kb, vb, O.k_bits, O.v_bits)
+        O.use_bridged_cache(kb, vb)
     t0 = cfg.N - cfg.Tq
     needles = {}
     for (b, t, h, p) in wl.needles:
@@ -41,7 +55,7 @@ def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=
     tol = tol_for(cfg.kv_dtype)
     idx_oracle = idx_h.copy()         # rows not sampled keep the HIP path's own indices
     stats = {"mismatch": 0, "o_err": 0.0, "score_err": 0.0}
-    for (b, i) in rows:
+    for ri, (b, i) in enumerate(rows):
         o_o, idx_o, sc_o = O.full_row(b, i)
         t = int(wl.q_pos[b, i])
         st = check_indices(idx_h[b, i], idx_o, sc_o, t, cfg.k_global, cfg.window, needles.get((b, i), []))
@@ -49,15 +63,15 @@ def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=
         err = float(np.max(np.abs(o_h[b, i] - o_o)))
         stats["o_err"] = max(stats["o_err"], err)
         assert err <= tol, f"row {(b, i)}: full-layer o error {err:.3e} > {tol}"
-        if dbg_h is not None:
+        if dbg_rows is not None:
             C = sc_o.shape[0]
             if C:
                 # fp32 logits carry a relative error: bound |d score| by score_tol + 1e-5 * score
-                dsc = np.abs(dbg_h[b, i, :C] - sc_o)
+                dsc = np.abs(dbg_rows[ri, :C] - sc_o)
                 serr = float(np.max(dsc))
                 stats["score_err"] = max(stats["score_err"], serr)
                 assert np.all(dsc <= score_tol + 1e-5 * sc_o), f"row {(b, i)}: score error {serr:.3e}"
-            assert np.all(dbg_h[b, i, C:] == -1.0)
+            assert np.all(dbg_rows[ri, C:] == -1.0)
         idx_oracle[b, i] = idx_o
     idx_dev = to_dev(idx_oracle, "i32")
     nl = cfg.n_sparse if sparse_layers is None else sparse_layers
@@ -68,6 +82,12 @@ def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=
                 ref = O.sparse_row(layer, b, i, idx_oracle[b, i])
                 err = float(np.max(np.abs(o_sp[b, i] - ref)))
                 assert err <= tol, f"sparse layer {layer} row {(b, i)} ws={ws}: error {err:.3e} > {tol}"
+        # the other direction: the HIP path on its own indices, the oracle on the same indices
+        o_own = g.sparse(layer, idx, workspace=True).cpu().numpy()
+        for (b, i) in rows:
+            ref = O.sparse_row(layer, b, i, idx_h[b, i])
+            err = float(np.max(np.abs(o_own[b, i] - ref)))
+            assert err <= tol, f"sparse layer {layer} row {(b, i)} on its own indices: error {err:.3e} > {tol}"
     _say(f"[parity] {cfg.name} ok: rows={len(rows)} band-mismatches={stats['mismatch']} "
          f"o_err={stats['o_err']:.2e} score_err={stats['score_err']:.2e}")
     return g, wl, idx, O
@@ -242,7 +262,7 @@ def test_bridge_one_row_random():
         wvb = f32_to_bf16_bits((rng.standard_normal((D, d)) * 0.02).astype(np.float32))
         k, v = hs2.hs2_kv_bridge(to_dev(hb, "bf16"), to_dev(wkb, "bf16"), to_dev(wvb, "bf16"))
         ko, vo = oracle.kv_bridge(hb, wkb, wvb)
-        check_bridge(hb, wkb, wvb, bits_from_dev(k), bits_from_dev(v), ko, vo, max_frac=None)
+        check_bridge(hb, wkb, wvb, bits_from_dev(k), bits_from_dev(v), ko, vo, rate_check=False)
 
 
 def test_bridge_strided_rows():
@@ -278,26 +298,36 @@ def test_full_decode1m_fp8():
     run_parity(CONFIGS["decode1m_fp8"], score_tol=1e-7)
 
 
-def _sample_rows(cfg, wl_needle_rows, n_extra=6, seed=0):
+def _chunk_rows(cfg, extra_rows, n_groups, n_random, seed):
+    """Rows of a full-size query chunk to check: the first and last row of n_groups of the chunk
+    kernel's 8-query workgroups spread over the chunk (including the first and the last
+    workgroup), the given rows, and n_random seeded rows."""
     rng = np.random.default_rng(seed)
-    rows = {(0, 0), (0, cfg.Tq - 1)}
-    rows.update(wl_needle_rows)
-    rows.update((0, int(i)) for i in rng.choice(cfg.Tq, size=n_extra, replace=False))
+    ngrp = cfg.Tq // 8
+    rows = set()
+    for gi in np.linspace(0, ngrp - 1, n_groups).round().astype(int):
+        rows.update({(0, 8 * int(gi)), (0, 8 * int(gi) + 7)})
+    rows.update(extra_rows)
+    rows.update((0, int(i)) for i in rng.choice(cfg.Tq, size=n_random, replace=False))
     return sorted(rows)
 
 
 def test_full_prefill_chunk_sampled():
+    """prefill_chunk: every needle row (all 64), the first and last row of 12 workgroups and 8 seeded
+    rows, with scores."""
     cfg = CONFIGS["prefill_chunk"]
     t0 = cfg.N - cfg.Tq
     from workloads.gen import _needle_plan
-    plan = _needle_plan(cfg)
-    needle_rows = [(0, plan[i][1] - t0) for i in (0, 17, 40, 63)]
-    run_parity(cfg, rows=_sample_rows(cfg, needle_rows), check_scores=False)
+    needle_rows = [(0, t - t0) for (_, t, _, _) in _needle_plan(cfg)]
+    rows = _chunk_rows(cfg, needle_rows, n_groups=12, n_random=8, seed=0)
+    assert len(rows) >= 64
+    run_parity(cfg, rows=rows, check_scores=True)
 
 
 def test_full_prefill_exit256k_sampled():
+    """prefill_exit256k: the bridge against the float64 projection, then the first and last row of
+    24 workgroups and 20 seeded rows of the chunk, with scores."""
     cfg = CONFIGS["prefill_exit256k"]
-    g, wl, _, O = run_parity(cfg, rows=_sample_rows(cfg, [], n_extra=4), check_scores=False)
-    # the bridge itself against the float64 projection
-    kb, vb = bits_from_dev(g.k[0]), bits_from_dev(g.v[0])
-    check_bridge(wl.hidden, wl.wk, wl.wv, kb, vb, O.k_bits, O.v_bits)
+    rows = _chunk_rows(cfg, [], n_groups=24, n_random=20, seed=1)
+    assert len(rows) >= 64
+    run_parity(cfg, rows=rows, check_scores=True)
