@@ -736,7 +736,7 @@ def main():
 # kernels of the full layer with its selection (the step minus the sparse layers and the bridge)
 FULL_SELECT_KERNELS = ("full_attn_mfma", "full_attn_combine", "full_attn_prefill", "full_attn_generic",
                        "score_rows_mfma", "score_prefill", "score_generic", "select_digit", "select_gather",
-                       "select_finish", "block_max", "block_select")
+                       "select_finish", "select_block_max", "select_blocks")
 
 
 def workload_record(cfg, res, args):
