@@ -125,6 +125,11 @@ SMALL = [
     # row's top digit found once by its own launch before the gather and finish
     small_config("rows72_many_seqs", 221, B=24, N=2500, Tq=3, n_sparse=1),
     small_config("rows66_fp8", 222, B=66, N=1800, Tq=1, kv_dtype="fp8", n_sparse=1),
+    # near-equal keys: distinct scores that all share the k-th's top radix digit, so the bucket
+    # overflows the candidate list and the finish takes its streaming passes with the picks
+    # spread over the whole row (decode rows and a query chunk)
+    small_config("near_ties_rows", 223, B=2, N=9000, Tq=1, n_sparse=1, near_ties=0.02),
+    small_config("near_ties_chunk", 224, B=1, N=7000, Tq=16, n_sparse=1, near_ties=0.02),
 ]
 
 

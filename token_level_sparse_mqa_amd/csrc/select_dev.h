@@ -410,11 +410,24 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
     }
 
     // ---- fallback: exact streaming passes over the row ----
+    // This path serves buckets of more than kSelCap entries, typically long runs of equal scores:
+    // a wave whose counted lanes all fall into one bin adds them with a single atomic.
+    auto hist_add = [&](bool pred, uint32_t bin) {
+        const uint64_t m = __ballot(pred);
+        if (!m) return;
+        const int lead = __ffsll((unsigned long long)m) - 1;
+        const uint32_t lb = __shfl(bin, lead);
+        if (__ballot(pred && bin != lb) == 0) {
+            if ((int)(threadIdx.x & 63) == lead) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
+        } else if (pred) {
+            atomicAdd(&hist[bin], 1u);
+        }
+    };
     for (int x = threadIdx.x; x < kHistBins; x += NT) hist[x] = 0;
     __syncthreads();
     for (int64_t j = threadIdx.x; j < C; j += NT) {
         const uint32_t key = __float_as_uint(sc[j]);
-        if (dig1(key) == b1) atomicAdd(&hist[dig2(key)], 1u);
+        hist_add(dig1(key) == b1, dig2(key));
     }
     __syncthreads();
     block_find_digit<NT>(hist, kHistBins, k1, b2, above2, tmp, res);
@@ -424,7 +437,7 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
     __syncthreads();
     for (int64_t j = threadIdx.x; j < C; j += NT) {
         const uint32_t key = __float_as_uint(sc[j]);
-        if ((key >> 10) == pre) atomicAdd(&hist[dig3(key)], 1u);
+        hist_add((key >> 10) == pre, dig3(key));
     }
     __syncthreads();
     block_find_digit<NT>(hist, 1024, k2, b3, above3, tmp, res);
@@ -445,6 +458,9 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
         if (pick && pos < (uint32_t)K) irow[pos] = (int32_t)j;
         run_eq += tot_eq;
         run_out += tot_pick;
+        // the picks number exactly K (everything above T and the lowest need_eq ties), so the
+        // pass ends once they are placed (early, when ties at T hold the low indices)
+        if (run_out >= (uint32_t)K) break;
     }
 }
 

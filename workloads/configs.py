@@ -33,6 +33,7 @@ class Config:
     needles: str = "none"  # "none" | "seeded8" | "spread64"
     bridge_D: int = 0      # >0: K/V come from a KV-Bridge projection of hidden states [N, D]
     ident_keys: bool = False  # every K row equal (tie / closed-form edge case)
+    near_ties: float = 0.0    # >0: every K row = one shared row + near_ties * its own N(0, 1) row
 
     @property
     def S(self) -> int:
@@ -74,11 +75,11 @@ def get_config(name: str) -> Config:
 def small_config(name: str, cfg_id: int, *, B: int, N: int, Tq: int, H: int = 32, d: int = 128,
                  q_dtype: str = "bf16", kv_dtype: str = "bf16", n_sparse: int = 1,
                  k_global: int = 1024, window: int = 128, needles: str = "none",
-                 bridge_D: int = 0, ident_keys: bool = False,
+                 bridge_D: int = 0, ident_keys: bool = False, near_ties: float = 0.0,
                  base: Optional[Config] = None) -> Config:
     """A reduced workload for parity tests (sizes the oracle finishes in seconds)."""
     if base is not None:
         return replace(base, name=name, cfg_id=cfg_id, B=B, N=N, Tq=Tq)
     return Config(name, cfg_id, B=B, N=N, Tq=Tq, H=H, d=d, q_dtype=q_dtype, kv_dtype=kv_dtype,
                   n_sparse=n_sparse, k_global=k_global, window=window, needles=needles,
-                  bridge_D=bridge_D, ident_keys=ident_keys)
+                  bridge_D=bridge_D, ident_keys=ident_keys, near_ties=near_ties)

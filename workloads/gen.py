@@ -150,6 +150,8 @@ def make_workload(cfg: Config) -> Workload:
     v32 = _normal(rng_for(cfg.cfg_id, T_V), (B, N, d))
     if cfg.ident_keys:
         k32[:] = k32[:, :1, :]
+    elif cfg.near_ties > 0:
+        k32 = (k32[:, :1, :] + np.float32(cfg.near_ties) * k32).astype(np.float32)
     if cfg.kv_dtype == "fp8":
         wl.k, wl.k_scale = quantize_fp8_rows(k32)
         wl.v, wl.v_scale = quantize_fp8_rows(v32)
