@@ -37,9 +37,11 @@ __global__ __launch_bounds__(64) void select_digit_kernel(SelectArgs a) {
     }
 }
 
-// seven waves per SIMD: long query chunks run tens of thousands of these workgroups
+// seven waves per SIMD for launches of many rows (query chunks run tens of thousands of these
+// workgroups, which take their digit from select_digit_kernel); launches of a few long rows (decode)
+// search the digit in every wave and hold the row histogram in registers meanwhile
 template <bool GIVEN>
-__global__ __launch_bounds__(256, 7) void select_gather_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256, GIVEN ? 7 : 4) void select_gather_kernel(SelectArgs a) {
     __shared__ GatherLds S;
     select_gather_body<GIVEN>(a, blockIdx.x, blockIdx.y, S);
 }

@@ -34,17 +34,25 @@ __device__ __forceinline__ uint32_t dig3(uint32_t key) { return key & 0x3ffu; }
 // digits NBINS-1-l*PER .. NBINS-(l+1)*PER, a shuffle scan over the lanes gives each lane the
 // count above its digits, and the lane that holds the k-th entry broadcasts it.  Should the
 // histogram hold fewer than k entries, digit 0 is reported (callers bound their writes).
+// Split in two so that callers can issue the histogram loads early: wave_load_hist reads this
+// lane's NBINS/64 digits, wave_digit_from searches them.
 template <int NBINS>
-__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k, uint32_t& digit, uint32_t& above) {
+__device__ __forceinline__ void wave_load_hist(const uint32_t* hist, uint32_t (&c)[NBINS / 64]) {
     constexpr int PER = NBINS / 64;
     const int lane = threadIdx.x & 63;
     const uint32_t* hb = hist + NBINS - (lane + 1) * PER;   // this lane's digits, ascending
-    uint32_t c[PER];
 #pragma unroll
     for (int i = 0; i < PER; i += 4) {
         const uint4 q = *(const uint4*)(hb + i);
         c[i] = q.x; c[i + 1] = q.y; c[i + 2] = q.z; c[i + 3] = q.w;
     }
+}
+
+template <int NBINS>
+__device__ __forceinline__ void wave_digit_from(const uint32_t (&c)[NBINS / 64], uint32_t k, uint32_t& digit,
+                                                uint32_t& above) {
+    constexpr int PER = NBINS / 64;
+    const int lane = threadIdx.x & 63;
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) local += c[i];
@@ -72,6 +80,13 @@ __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k
         digit = 0;
         above = total - __shfl(c[0], 63);    // lane 63 holds digits PER-1 .. 0
     }
+}
+
+template <int NBINS>
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t k, uint32_t& digit, uint32_t& above) {
+    uint32_t c[NBINS / 64];
+    wave_load_hist<NBINS>(hist, c);
+    wave_digit_from<NBINS>(c, k, digit, above);
 }
 
 // Block-level digit search for a histogram in LDS: thread t reads consecutive digits (no bank
@@ -131,22 +146,31 @@ struct GatherLds {
 template <bool GIVEN = false>
 __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, int seg, GatherLds& S) {
     constexpr int PER = kSelSeg / 256;
+    // the segment's scores (every position below Nmax is inside the row's buffer; those past the
+    // candidate count are masked below) and the row histogram or digit are loaded together with
+    // the row's position: one memory round trip before the classification
+    const int64_t j0 = (int64_t)seg * kSelSeg;
+    const float* sc = a.scores + (int64_t)r * a.cstride;
+    uint32_t key[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int64_t j = j0 + u * 256 + threadIdx.x;
+        key[u] = j < a.Nmax ? __float_as_uint(sc[j]) : 0u;
+    }
+    uint32_t hc[kHistBins / 64];
+    uint32_t b1 = 0, above1;
+    if constexpr (GIVEN) b1 = a.digits[2 * (int64_t)r];
+    else wave_load_hist<kHistBins>(a.rowhist + (int64_t)r * kHistBins, hc);
     int64_t t, C;
     row_info(a, r, &t, &C);
     if (C <= a.k_global) return;
-    const int64_t j0 = (int64_t)seg * kSelSeg;
     if (j0 >= C) return;
     const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
-    uint32_t b1, above1;
-    if constexpr (GIVEN) b1 = a.digits[2 * (int64_t)r];
-    else wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)a.k_global, b1, above1);
-    const float* sc = a.scores + (int64_t)r * a.cstride;
-    uint32_t key[PER];
+    if constexpr (!GIVEN) wave_digit_from<kHistBins>(hc, (uint32_t)a.k_global, b1, above1);
     uint32_t ns = 0, nc = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int64_t j = j0 + u * 256 + threadIdx.x;
-        key[u] = j < j1 ? __float_as_uint(sc[j]) : 0u;
         const uint32_t dg = dig1(key[u]);
         ns += (j < j1 && dg > b1) ? 1u : 0u;
         nc += (j < j1 && dg == b1) ? 1u : 0u;
@@ -285,6 +309,33 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
     uint32_t (&lcount)[2] = S.lcount;
 
     const int K = a.k_global, W = a.window;
+    // Every global load of the row is issued before any is used, so together they cost one memory
+    // round trip: the candidate slots, the candidate count, the sure list, the row histogram (or
+    // the row's digit) and the row's position.  All lie at fixed, in-bounds addresses; slots past
+    // the counts hold stale values that are never used.
+    constexpr int CU = kSelCap / NT;
+    const uint2* cg = a.cand + (int64_t)r * kSelCap;
+    uint2 cpre[CU];
+#pragma unroll
+    for (int u = 0; u < CU; ++u) cpre[u] = cg[threadIdx.x + u * NT];
+    const uint32_t n_cand = a.counters[(int64_t)r * 4 + 1];
+    constexpr int SU = (4096 + NT - 1) / NT;       // sure slots per thread (k_global <= 4096)
+    int32_t spre[SU];
+#pragma unroll
+    for (int u = 0; u < SU; ++u) {
+        const int x = threadIdx.x + u * NT;
+        spre[u] = a.sure[(int64_t)r * K + (x < K ? x : K - 1)];
+    }
+    constexpr int HU = kHistBins / NT;
+    uint32_t hpre[HU];
+    uint32_t b1 = 0, above1 = 0;
+    if constexpr (GIVEN) {
+        b1 = a.digits[2 * (int64_t)r];
+        above1 = a.digits[2 * (int64_t)r + 1];
+    } else {
+#pragma unroll
+        for (int u = 0; u < HU; ++u) hpre[u] = a.rowhist[(int64_t)r * kHistBins + threadIdx.x + u * NT];
+    }
     int64_t t, C;
     row_info(a, r, &t, &C);
     int32_t* irow = a.idx + (int64_t)r * (K + W);
@@ -292,14 +343,12 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
 
     // window segment and the optional score dump
     for (int w = threadIdx.x; w < W; w += NT) {
-        const int64_t j = t - W + 1 + w;
         int32_t v = -1;
         if (t >= 0) {
             const int64_t first = t - W + 1 > 0 ? t - W + 1 : 0;
             const int64_t jj = first + w;
             v = jj <= t ? (int32_t)jj : -1;
         }
-        (void)j;
         irow[K + w] = v;
     }
     if (a.scores_dbg) {
@@ -310,23 +359,13 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
         for (int j = threadIdx.x; j < K; j += NT) irow[j] = j < C ? j : -1;
         return;
     }
-
-    // every candidate slot the fast path may use is loaded before the digit search, so these
-    // loads, the candidate count and the histogram reads are in flight together (slots past the
-    // count hold stale values that are never used)
-    constexpr int CU = kSelCap / NT;
-    const uint2* cg = a.cand + (int64_t)r * kSelCap;
-    uint2 cpre[CU];
+    if constexpr (!GIVEN) {
+        // the k-th's top digit from the row histogram, staged in LDS (the block search ends with a
+        // barrier, after which the histogram space is free for the next digits)
 #pragma unroll
-    for (int u = 0; u < CU; ++u) cpre[u] = cg[threadIdx.x + u * NT];
-    const uint32_t* cnt = a.counters + (int64_t)r * 4;
-    const uint32_t n_cand = cnt[1];
-    uint32_t b1, above1;
-    if constexpr (GIVEN) {
-        b1 = a.digits[2 * (int64_t)r];
-        above1 = a.digits[2 * (int64_t)r + 1];
-    } else {
-        wave_find_digit<kHistBins>(a.rowhist + (int64_t)r * kHistBins, (uint32_t)K, b1, above1);
+        for (int u = 0; u < HU; ++u) hist[threadIdx.x + u * NT] = hpre[u];
+        __syncthreads();
+        block_find_digit<NT>(hist, kHistBins, (uint32_t)K, b1, above1, tmp, res);
     }
     const uint32_t k1 = (uint32_t)K - above1;
     uint32_t b2, b3, above2, above3;
@@ -355,7 +394,11 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
         const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
         // sure picks from the gather pass
         const uint32_t n_sure = above1 < (uint32_t)K ? above1 : (uint32_t)K;
-        for (uint32_t x = threadIdx.x; x < n_sure; x += NT) out[x] = a.sure[(int64_t)r * K + x];
+#pragma unroll
+        for (int u = 0; u < SU; ++u) {
+            const uint32_t x = threadIdx.x + u * NT;
+            if (x < n_sure) out[x] = spre[u];
+        }
         if (threadIdx.x == 0) { lcount[0] = n_sure; lcount[1] = 0; }
         // classify the bucket: above T -> picked; equal to T -> tie list (reusing ckey storage)
         uint32_t myk[kSelCap / NT];
