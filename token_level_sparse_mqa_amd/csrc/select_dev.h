@@ -466,39 +466,73 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
             atomicAdd(&hist[bin], 1u);
         }
     };
+    // The row's scores are read UB positions per thread at a time, all of a batch's loads in flight
+    // together (one memory round trip per NT * UB positions).
+    constexpr int UB = 4;
+    auto hist_pass = [&](auto count) {
+        for (int64_t jb = 0; jb < C; jb += (int64_t)NT * UB) {
+            uint32_t kk[UB];
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const int64_t j = jb + (int64_t)u * NT + threadIdx.x;
+                kk[u] = j < C ? __float_as_uint(sc[j]) : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < UB; ++u) count(jb + (int64_t)u * NT + threadIdx.x < C, kk[u]);
+        }
+    };
     for (int x = threadIdx.x; x < kHistBins; x += NT) hist[x] = 0;
     __syncthreads();
-    for (int64_t j = threadIdx.x; j < C; j += NT) {
-        const uint32_t key = __float_as_uint(sc[j]);
-        hist_add(dig1(key) == b1, dig2(key));
-    }
+    hist_pass([&](bool valid, uint32_t key) { hist_add(valid && dig1(key) == b1, dig2(key)); });
     __syncthreads();
     block_find_digit<NT>(hist, kHistBins, k1, b2, above2, tmp, res);
     const uint32_t k2 = k1 - above2;
     const uint32_t pre = (b1 << 11) | b2;
     for (int x = threadIdx.x; x < kHistBins; x += NT) hist[x] = 0;
     __syncthreads();
-    for (int64_t j = threadIdx.x; j < C; j += NT) {
-        const uint32_t key = __float_as_uint(sc[j]);
-        hist_add((key >> 10) == pre, dig3(key));
-    }
+    hist_pass([&](bool valid, uint32_t key) { hist_add(valid && (key >> 10) == pre, dig3(key)); });
     __syncthreads();
     block_find_digit<NT>(hist, 1024, k2, b3, above3, tmp, res);
     const uint32_t need_eq = k2 - above3;
     const uint32_t T = (b1 << 21) | (b2 << 10) | b3;
-    // ordered pass: ties ranked by index with a running block scan
+    // ordered pass: thread t takes the UB consecutive positions jb + UB t .. jb + UB t + UB - 1, so
+    // thread order is position order; a block scan of the per-thread tie counts ranks the ties by
+    // index, a second one places the picks
     uint32_t run_eq = 0, run_out = 0;
-    for (int64_t jb = 0; jb < C; jb += NT) {
-        const int64_t j = jb + threadIdx.x;
-        uint32_t key = 0;
-        if (j < C) key = __float_as_uint(sc[j]);
-        const bool eq = j < C && key == T;
+    for (int64_t jb = 0; jb < C; jb += (int64_t)NT * UB) {
+        const int64_t jt = jb + (int64_t)threadIdx.x * UB;
+        uint32_t kk[UB];
+#pragma unroll
+        for (int u = 0; u < UB; ++u) kk[u] = jt + u < C ? __float_as_uint(sc[jt + u]) : 0u;
+        uint32_t neq = 0;
+#pragma unroll
+        for (int u = 0; u < UB; ++u) neq += (jt + u < C && kk[u] == T) ? 1u : 0u;
         uint32_t tot_eq;
-        const uint32_t rank = run_eq + block_excl_scan<NT>(eq ? 1u : 0u, tmp, &tot_eq);
-        const bool pick = j < C && (key > T || (eq && rank < need_eq));
+        const uint32_t rank0 = run_eq + block_excl_scan<NT>(neq, tmp, &tot_eq);
+        uint32_t npick = 0;
+        {
+            uint32_t rank = rank0;
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const bool valid = jt + u < C, eq = valid && kk[u] == T;
+                npick += (valid && (kk[u] > T || (eq && rank < need_eq))) ? 1u : 0u;
+                rank += eq ? 1u : 0u;
+            }
+        }
         uint32_t tot_pick;
-        const uint32_t pos = run_out + block_excl_scan<NT>(pick ? 1u : 0u, tmp, &tot_pick);
-        if (pick && pos < (uint32_t)K) irow[pos] = (int32_t)j;
+        uint32_t pos = run_out + block_excl_scan<NT>(npick, tmp, &tot_pick);
+        {
+            uint32_t rank = rank0;
+#pragma unroll
+            for (int u = 0; u < UB; ++u) {
+                const bool valid = jt + u < C, eq = valid && kk[u] == T;
+                if (valid && (kk[u] > T || (eq && rank < need_eq))) {
+                    if (pos < (uint32_t)K) irow[pos] = (int32_t)(jt + u);
+                    ++pos;
+                }
+                rank += eq ? 1u : 0u;
+            }
+        }
         run_eq += tot_eq;
         run_out += tot_pick;
         // the picks number exactly K (everything above T and the lowest need_eq ties), so the
