@@ -167,14 +167,18 @@ __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, i
     if (j0 >= C) return;
     const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
     if constexpr (!GIVEN) wave_digit_from<kHistBins>(hc, (uint32_t)a.k_global, b1, above1);
-    uint32_t ns = 0, nc = 0;
+    // bit u of sm / cm: entry u is a sure pick / a bucket candidate (kept in vector registers, so
+    // the sixteen per-entry conditions need no lane masks across the reservation below)
+    const int nvalid = (int)(j1 - j0);
+    uint32_t sm = 0, cm = 0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int64_t j = j0 + u * 256 + threadIdx.x;
+        const bool valid = u * 256 + (int)threadIdx.x < nvalid;
         const uint32_t dg = dig1(key[u]);
-        ns += (j < j1 && dg > b1) ? 1u : 0u;
-        nc += (j < j1 && dg == b1) ? 1u : 0u;
+        sm |= (valid && dg > b1) ? (1u << u) : 0u;
+        cm |= (valid && dg == b1) ? (1u << u) : 0u;
     }
+    const uint32_t ns = (uint32_t)__popc(sm), nc = (uint32_t)__popc(cm);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint32_t mine = (ns << 16) | nc;
     uint32_t incl = mine;
@@ -208,18 +212,18 @@ __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, i
     const uint32_t excl = incl - mine;
     uint32_t ps = S.wbase[w][0] + (excl >> 16);
     uint32_t pc = S.wbase[w][1] + (excl & 0xffffu);
+    int32_t* sure = a.sure + (int64_t)r * a.k_global;
+    uint2* cand = a.cand + (int64_t)r * kSelCap;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-        const int64_t j = j0 + u * 256 + threadIdx.x;
-        if (j >= j1) continue;
-        const uint32_t dg = dig1(key[u]);
-        if (dg > b1) {
+        const int32_t j = (int32_t)(j0 + u * 256 + threadIdx.x);
+        if ((sm >> u) & 1u) {
             // fewer than k_global entries lie above the k-th's bucket; the bound only matters
             // if the row histogram disagreed with the scores
-            if (ps < (uint32_t)a.k_global) a.sure[(int64_t)r * a.k_global + ps] = (int32_t)j;
+            if (ps < (uint32_t)a.k_global) sure[ps] = j;
             ++ps;
-        } else if (dg == b1) {
-            if (pc < (uint32_t)kSelCap) a.cand[(int64_t)r * kSelCap + pc] = make_uint2(key[u], (uint32_t)j);
+        } else if ((cm >> u) & 1u) {
+            if (pc < (uint32_t)kSelCap) cand[pc] = make_uint2(key[u], (uint32_t)j);
             ++pc;
         }
     }
@@ -467,7 +471,7 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
         }
     };
     // The row's scores are read UB positions per thread at a time, all of a batch's loads in flight
-    // together (one memory round trip per NT * UB positions).
+    // together (one memory round trip per NT * UB positions; eight per thread measured slower).
     constexpr int UB = 4;
     auto hist_pass = [&](auto count) {
         for (int64_t jb = 0; jb < C; jb += (int64_t)NT * UB) {
