@@ -40,9 +40,6 @@ bool dtype_pair_ok(int qd, int kd) {
 
 // ---- workspace plan of hs2_full_attn_select ----------------------------------------------------
 enum Path { PATH_GENERIC = 0, PATH_MFMA_ROWS = 1, PATH_MFMA_PREFILL = 2 };
-// query tokens per sequence from which the chunk kernels (8 queries sharing each K/V tile)
-// replace the one-row-per-workgroup kernels
-constexpr int kPrefillMinTq = 8;
 // The chunk kernels address a sequence's cache rows with 32-bit byte offsets: they take the
 // chunk only when Nmax rows of K (or V) span less than 2^31 bytes (8M keys at d = 128 in bf16);
 // longer caches take the row kernels, whose offsets are 64-bit.

@@ -44,10 +44,11 @@ struct RowTile {
 // LIST: `ids` holds the workgroup's key ids in LDS; otherwise (range mode) key = entry.
 // Cache policy, measured on MI355X: in range mode (the full layer) K is loaded normally and V
 // non-temporally, so V's lines do not displace K's from the memory-side cache before the score
-// pass reads K again (decode128k: attention 103.5 -> 87 us, score pass 53.8 -> 47 us); in list
-// mode (the sparse layers) both are gathered non-temporally (cold 1152-row gathers of 256
-// queries: 79 -> 49 us).
-template <int D, int KV, bool LIST>
+// pass reads K again (decode128k: attention 103.5 -> 87 us, score pass 53.8 -> 47 us).  In list
+// mode (the sparse layers) decode rows gather both non-temporally (cold 1152-row gathers of 256
+// queries: 79 -> 49 us), while query chunks (REUSE), whose queries share window rows and
+// often-chosen keys of one sequence, gather with cached loads (prefill_chunk: 380 -> 251 us).
+template <int D, int KV, bool LIST, bool REUSE = false>
 __device__ __forceinline__ void load_row_tile(RowTile<D, KV>& T, const AttnArgs& a, int64_t rowbase, int64_t L,
                                               int64_t e_lo, int64_t e_hi, int64_t tile_e, const int32_t* ids) {
     const int lane = threadIdx.x & 63;
@@ -65,8 +66,8 @@ __device__ __forceinline__ void load_row_tile(RowTile<D, KV>& T, const AttnArgs&
     // a masked key reads the last key of the range (range mode) or row 0 (list mode)
     const int32_t jr = (int32_t)(j >= 0 ? j : (LIST ? 0 : e_hi - 1));
     auto src = [&](int R) { return rowbase + __shfl(jr, R); };
-    load_raw_tile<D, KV, LIST>(T.k, a.k, src);
-    load_raw_tile<D, KV, true>(T.v, a.v, src);
+    load_raw_tile<D, KV, LIST && !REUSE>(T.k, a.k, src);
+    load_raw_tile<D, KV, !(LIST && REUSE)>(T.v, a.v, src);
     if (KV == HS2_FP8_E4M3) {
         T.ks = a.k_scale[rowbase + jr];
         T.vs = a.v_scale[rowbase + jr];
@@ -192,7 +193,7 @@ struct RowLds {
 
 // One workgroup's work: block row bx (row, or layer * R + row), key split `split`.  LIST: the
 // keys are the index list a.list (sparse layers), otherwise the causal range (the full layer).
-template <int D, int KV, bool LIST>
+template <int D, int KV, bool LIST, bool REUSE = false>
 __device__ __forceinline__ void attn_rows_body(const AttnArgs& a, int bx, int split, RowLds<D>& S) {
     constexpr int NW = kRowWaves;
     constexpr int NT = NW * 64;
@@ -282,10 +283,10 @@ __device__ __forceinline__ void attn_rows_body(const AttnArgs& a, int bx, int sp
     const int64_t ntw = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles of this wave
     if (ntw > 0) {
         auto tile_e = [&](int64_t it) { return e0 + 32 * (w + (int64_t)NW * it); };
-        load_row_tile<D, KV, LIST>(T, a, rowbase, L, e0, e1, tile_e(0), ids);
+        load_row_tile<D, KV, LIST, REUSE>(T, a, rowbase, L, e0, e1, tile_e(0), ids);
         for (int64_t it = 0; it + 1 < ntw; ++it) {
             const uint32_t valid = stage_row_tile<D, KV>(T, W);
-            load_row_tile<D, KV, LIST>(T, a, rowbase, L, e0, e1, tile_e(it + 1), ids);
+            load_row_tile<D, KV, LIST, REUSE>(T, a, rowbase, L, e0, e1, tile_e(it + 1), ids);
             wave_lds_fence();
             row_tile_step<D, KV>(W, valid, S.q, oacc, m_run, l_run, sl2);
             wave_lds_fence();

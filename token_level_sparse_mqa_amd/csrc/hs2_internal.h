@@ -19,6 +19,10 @@ constexpr int kSelSeg = 4096;
 constexpr int kSelDigitRows = 64;     // rows from which a launch finds each row's digit once
 static_assert(HS2_MAX_SELECT_NMAX == (int64_t)65535 * kSelSeg, "one selection segment per grid row, at most 65535");
 constexpr int kBlkMaxCand = 16384;   // candidate blocks per row of the block-level selection
+// Query tokens per sequence from which a launch is a query chunk: the full layer takes the chunk
+// kernels (8 queries sharing each K/V tile) instead of one row per workgroup, and the sparse layers
+// gather with cached loads (the chunk's queries share window rows and often-chosen keys).
+constexpr int kPrefillMinTq = 8;
 
 // One attention problem: R = B*Tq query rows, each over a key set given either as the causal
 // range [0, t] (list == nullptr) or as an index list idx[r, 0:S].
