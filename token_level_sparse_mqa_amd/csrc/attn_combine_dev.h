@@ -42,9 +42,11 @@ struct CombineWideLds {
     float wred[4];
 };
 
-// One workgroup of 256 threads: block row bx, head h, dims 16 bz .. 16 bz + 15.
-template <int D>
-__device__ __forceinline__ void combine_wide_body(const AttnArgs& a, int bx, int h, int bz, CombineWideLds& S) {
+// One workgroup of 256 threads: block row bx, head h, dims 16 bz .. 16 bz + 15.  SK (m, l) pairs
+// per thread and the first U0 splits per output dim are loaded up front (sized to the split count,
+// so that no load is a clamped repeat).
+template <int D, int SK, int U0>
+__device__ __forceinline__ void combine_wide_impl(const AttnArgs& a, int bx, int h, int bz, CombineWideLds& S) {
     float (&red)[16][17] = S.red;
     float (&wred)[4] = S.wred;
     const CombineRow cr = combine_row(a, bx);
@@ -54,30 +56,60 @@ __device__ __forceinline__ void combine_wide_body(const AttnArgs& a, int bx, int
     const float* obase = cr.part + ((int64_t)r * ns * H + h) * D;
     const float* mbase = cr.part_ml + ((int64_t)r * ns * H + h) * 2;
     const int64_t ostride = (int64_t)H * D, mstride = (int64_t)H * 2;
+    const int dl = tid & 15, sl = tid >> 4;
+    const int dv = bz * 16 + dl;
+    // Every load that does not depend on the maximum is issued before the first reduction: the
+    // (m, l) pairs of this thread's splits tid + 256 k and the first U0 splits sl + 16 u of its
+    // output dim (loads are clamped to the last split and masked where used), so up to 256 splits
+    // cost one round trip instead of three.
+    float2 st[SK];
+#pragma unroll
+    for (int k = 0; k < SK; ++k) {
+        const int s = tid + 256 * k;
+        st[k] = *(const float2*)(mbase + (int64_t)(s < ns ? s : ns - 1) * mstride);
+    }
+    float mu0[U0], ou0[U0];
+#pragma unroll
+    for (int u = 0; u < U0; ++u) {
+        const int s = sl + 16 * u < ns ? sl + 16 * u : ns - 1;
+        mu0[u] = mbase[s * mstride];
+        ou0[u] = obase[s * ostride + dv];
+    }
     float m = kNegInf;
-    for (int s = tid; s < ns; s += 256) m = fmaxf(m, mbase[s * mstride]);
+    for (int k = 0; k < SK; ++k)
+        if (tid + 256 * k < ns) m = fmaxf(m, st[k].x);
+    for (int s = tid + 256 * SK; s < ns; s += 256) m = fmaxf(m, mbase[s * mstride]);
     m = wave_max(m);
     if (lane == 0) wred[wv] = m;
     __syncthreads();
     const float M = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
     __syncthreads();
     float l = 0.f;
-    if (M != kNegInf)
-        for (int s = tid; s < ns; s += 256) {
+    if (M != kNegInf) {
+#pragma unroll
+        for (int k = 0; k < SK; ++k)
+            if (tid + 256 * k < ns && st[k].x != kNegInf) l += st[k].y * exp2f(st[k].x - M);
+        for (int s = tid + 256 * SK; s < ns; s += 256) {
             const float ms = mbase[s * mstride];
             l += ms == kNegInf ? 0.f : mbase[s * mstride + 1] * exp2f(ms - M);
         }
+    }
     l = wave_sum(l);
     if (lane == 0) wred[wv] = l;
     __syncthreads();
     const float Ltot = wred[0] + wred[1] + wred[2] + wred[3];
-    const int dl = tid & 15, sl = tid >> 4;
-    const int dv = bz * 16 + dl;
     float acc = 0.f;
     if (M != kNegInf) {
-        // batches of U splits per thread with all their loads in flight together (16, then 8),
-        // so a long row's merge takes one or two round trips instead of one per four splits
-        int s = sl;
+        {
+            float part = 0.f;
+#pragma unroll
+            for (int u = 0; u < U0; ++u)
+                part += (sl + 16 * u < ns && mu0[u] != kNegInf) ? ou0[u] * exp2f(mu0[u] - M) : 0.f;
+            acc += part;
+        }
+        // the remaining splits in batches of U per thread with all their loads in flight together
+        // (16, then 8), so a long row's merge takes a few round trips instead of one per four splits
+        int s = sl + 16 * U0;
         auto batch = [&](auto u_c) {
             constexpr int U = decltype(u_c)::value;
             for (; s + 16 * (U - 1) < ns; s += 16 * U) {
@@ -110,6 +142,14 @@ __device__ __forceinline__ void combine_wide_body(const AttnArgs& a, int bx, int
         cr.o[((int64_t)r * H + h) * D + dvo] = Ltot > 0.f ? tot / Ltot : 0.f;
         if (dvo == 0 && cr.lse) cr.lse[(int64_t)r * H + h] = Ltot > 0.f ? M + log2f(Ltot) : kNegInf;
     }
+}
+
+template <int D>
+__device__ __forceinline__ void combine_wide_body(const AttnArgs& a, int bx, int h, int bz, CombineWideLds& S) {
+    if (a.nsplit <= 128) combine_wide_impl<D, 1, 8>(a, bx, h, bz, S);
+    else if (a.nsplit <= 256) combine_wide_impl<D, 1, 16>(a, bx, h, bz, S);
+    else if (a.nsplit <= 512) combine_wide_impl<D, 2, 16>(a, bx, h, bz, S);
+    else combine_wide_impl<D, 4, 16>(a, bx, h, bz, S);
 }
 
 // Few splits: one workgroup per (row, head), one thread per dv.  Splits are merged in batches of 16 whose
