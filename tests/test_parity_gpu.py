@@ -20,14 +20,15 @@ pytestmark = pytest.mark.gpu
 
 
 
-def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=1e-7):
+def run_parity(cfg, rows=None, check_scores=True, sparse_layers=None, score_tol=1e-7, wl=None):
     """The full layer, the selection and the sparse layers of one workload against the oracle on
     the given rows (default: every row).  The sparse layers are checked both ways (reading R12):
     the HIP path on the oracle's indices, and the HIP path on its own indices against the oracle
-    on those same indices."""
+    on those same indices.  `wl` replaces the workload generated from cfg."""
     _say(f"[parity] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} H={cfg.H} d={cfg.d} "
          f"{cfg.q_dtype}/{cfg.kv_dtype} k={cfg.k_global} W={cfg.window}")
-    wl = make_workload(cfg)
+    if wl is None:
+        wl = make_workload(cfg)
     g = HipRun(wl)
     if cfg.bridge_D:
         g.bridge()
@@ -336,3 +337,49 @@ def test_full_prefill_exit256k_sampled():
     rows = _chunk_rows(cfg, [], n_groups=24, n_random=20, seed=1)
     assert len(rows) >= 64
     run_parity(cfg, rows=rows, check_scores=True)
+
+
+def varlen_workload(cfg, lengths):
+    """cfg's workload with sequences of different lengths: sequence b holds lengths[b] valid cache
+    rows, its queries are the last Tq positions of those, and every cache row past its length is
+    NaN (K and V; for FP8 the codes and the row scales), so a kernel that read past kv_len, or let
+    a masked row's data into a product, would put NaN into the outputs."""
+    wl = make_workload(cfg)
+    L = np.asarray(lengths, dtype=np.int32)
+    assert L.shape == (cfg.B,) and np.all(L <= cfg.N) and np.all(L >= cfg.Tq)
+    wl.kv_len = L.copy()
+    wl.q_pos = (L[:, None] - cfg.Tq + np.arange(cfg.Tq, dtype=np.int32)[None, :]).astype(np.int32)
+    for b, n in enumerate(L):
+        if cfg.kv_dtype == "bf16":
+            wl.k[b, n:] = 0x7FC0
+            wl.v[b, n:] = 0x7FC0
+        elif cfg.kv_dtype == "fp8":
+            wl.k[b, n:] = 0x7F
+            wl.v[b, n:] = 0x7F
+            wl.k_scale[b, n:] = np.nan
+            wl.v_scale[b, n:] = np.nan
+        else:
+            wl.k[b, n:] = np.nan
+            wl.v[b, n:] = np.nan
+    return wl
+
+
+VARLEN = [
+    # decode rows: one full-length sequence, one mid-length, one just above k + W candidates
+    (small_config("varlen_rows", 240, B=3, N=4000, Tq=2, n_sparse=1), [4000, 2600, 1300]),
+    (small_config("varlen_fp8", 241, B=2, N=5000, Tq=1, kv_dtype="fp8", n_sparse=1), [3100, 5000]),
+    (small_config("varlen_f32", 242, B=2, N=1500, Tq=2, H=16, d=64, q_dtype="f32", kv_dtype="f32",
+                  n_sparse=1), [1500, 1200]),
+    # query chunks: the 8-query workgroups stop at their own sequence's last row
+    (small_config("varlen_chunk", 243, B=2, N=3000, Tq=24, n_sparse=1), [3000, 1900]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: c[0].name)
+def test_varlen_poisoned_tail(case):
+    cfg, lengths = case
+    g, wl, idx, O = run_parity(cfg, wl=varlen_workload(cfg, lengths))
+    # every index lies below its own sequence's length
+    idx_h = idx.cpu().numpy()
+    for b, n in enumerate(lengths):
+        assert np.all(idx_h[b] < n)
