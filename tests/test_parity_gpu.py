@@ -383,3 +383,55 @@ def test_varlen_poisoned_tail(case):
     idx_h = idx.cpu().numpy()
     for b, n in enumerate(lengths):
         assert np.all(idx_h[b] < n)
+
+
+SPARSE_LISTS = [("bf16", 300), ("bf16", 1152), ("fp8", 777)]
+
+
+@pytest.mark.parametrize("kv, S", SPARSE_LISTS, ids=lambda x: str(x))
+def test_sparse_list_semantics(kv, S):
+    """hs2_sparse_attn on lists the selection never produces, against its documented semantics:
+    entries outside [0, min(kv_len, Nmax)) are skipped like -1 (including rows inside Nmax but past
+    the sequence's length), repeated entries count once per occurrence, and a row with no valid
+    entry gets o = 0.  The expected value filters the list by that rule and hands the rest to the
+    oracle's sparse attention; the split and the one-workgroup forms are both checked."""
+    cfg = small_config(f"sparse_lists_{kv}_{S}", 250 + S % 97 + (kv == "fp8"), B=2, N=3000, Tq=3,
+                       kv_dtype=kv, n_sparse=1)
+    _say(f"[sparse-lists] {cfg.name}")
+    wl = make_workload(cfg)
+    L = np.array([3000, 2200], dtype=np.int32)
+    wl.kv_len = L
+    rng = np.random.default_rng(cfg.cfg_id)
+    idx = np.empty((cfg.B, cfg.Tq, S), dtype=np.int32)
+    for b in range(cfg.B):
+        for i in range(cfg.Tq):
+            if (b, i) == (1, 2):
+                # nothing valid: -1, past this sequence's length but inside Nmax, past Nmax
+                row = rng.choice(np.array([-1, -7, int(L[1]), int(L[1]) + 5, cfg.N - 1, cfg.N, cfg.N + 7, 2 ** 30]),
+                                 size=S)
+            else:
+                row = rng.choice(cfg.N, size=S, replace=False).astype(np.int64)
+                u = rng.random(S)
+                row[u < 0.10] = -1                                     # holes
+                past = (u >= 0.10) & (u < 0.14)
+                row[past] = cfg.N + rng.integers(0, 1000, size=int(past.sum()))      # past Nmax
+                rep = (u >= 0.14) & (u < 0.19)                         # repeats of earlier entries
+                src = rng.integers(0, S, size=int(rep.sum()))
+                row[rep] = row[src]
+            idx[b, i] = row.astype(np.int32)
+    g = HipRun(wl)
+    O = OracleRun(wl)
+    tol = tol_for(cfg.kv_dtype)
+    idx_dev = to_dev(idx, "i32")
+    for ws in (True, False):
+        o = g.sparse(0, idx_dev, workspace=ws).cpu().numpy()
+        for b in range(cfg.B):
+            for i in range(cfg.Tq):
+                row = idx[b, i].astype(np.int64)
+                keep = row[(row >= 0) & (row < min(int(L[b]), cfg.N))]
+                ref = O.sparse_row(0, b, i, keep)
+                err = float(np.max(np.abs(o[b, i] - ref)))
+                assert err <= tol, f"ws={ws} row {(b, i)}: error {err:.3e} > {tol}"
+                if keep.shape[0] == 0:
+                    assert np.all(o[b, i] == 0.0)
+    _say(f"[sparse-lists] {cfg.name} ok")
