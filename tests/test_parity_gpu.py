@@ -435,3 +435,26 @@ def test_sparse_list_semantics(kv, S):
                 if keep.shape[0] == 0:
                     assert np.all(o[b, i] == 0.0)
     _say(f"[sparse-lists] {cfg.name} ok")
+
+
+SCATTERED = [
+    small_config("scattered_rows", 244, B=2, N=3000, Tq=5, n_sparse=1),
+    small_config("scattered_chunk", 245, B=1, N=3000, Tq=24, n_sparse=1),
+    small_config("scattered_chunk_fp8", 246, B=2, N=2500, Tq=16, kv_dtype="fp8", n_sparse=1),
+]
+
+
+@pytest.mark.parametrize("cfg", SCATTERED, ids=lambda c: c.name)
+def test_scattered_positions(cfg):
+    """Query positions in any order, not the last Tq of the sequence: unsorted, spread over the
+    whole sequence (some with fewer than k + W visible keys, one at position 0) and repeated, so
+    the 8-query workgroups of the chunk kernels span very different key ranges."""
+    wl = make_workload(cfg)
+    rng = np.random.default_rng(cfg.cfg_id)
+    pos = rng.integers(0, cfg.N, size=(cfg.B, cfg.Tq)).astype(np.int32)
+    pos[0, 0] = 0
+    pos[0, 1] = cfg.N - 1
+    pos[-1, -1] = pos[-1, 0]                    # a repeated position
+    pos[0, 2] = 700                             # fewer candidates than k
+    wl.q_pos = pos
+    run_parity(cfg, wl=wl)
