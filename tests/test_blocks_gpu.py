@@ -47,10 +47,11 @@ def check_block_row(bidx, idx, bid_o, idx_o, sc_o, t, kb, block, W, needles=()):
     return int(diff.size // 2)
 
 
-def run_block_parity(cfg, kb=16, block=64, rows=None, sparse=True):
+def run_block_parity(cfg, kb=16, block=64, rows=None, sparse=True, wl=None):
     _say(f"[blocks] {cfg.name} B={cfg.B} N={cfg.N} Tq={cfg.Tq} {cfg.q_dtype}/{cfg.kv_dtype} kb={kb} block={block}")
     import token_level_sparse_mqa_amd as hs2
-    wl = make_workload(cfg)
+    if wl is None:
+        wl = make_workload(cfg)
     g = HipRun(wl)
     if cfg.bridge_D:
         g.bridge()
@@ -142,3 +143,20 @@ def test_blocks_full_prefill_chunk_sampled():
     rows = sorted({(0, 0), (0, cfg.Tq - 1)} | {(0, plan[i][1] - t0) for i in (0, 21, 42, 63)} |
                   {(0, int(x)) for x in np.random.default_rng(1).choice(cfg.Tq, 4, replace=False)})
     run_block_parity(cfg, rows=rows)
+
+
+def test_blocks_varlen_and_scattered():
+    """Block selection on sequences of different lengths with NaN past each length, and on query
+    positions in any order (see the token-level tests of the same names)."""
+    from tests.test_parity_gpu import varlen_workload
+    cfg = small_config("blk_varlen", 256, B=3, N=4000, Tq=2, n_sparse=1)
+    run_block_parity(cfg, 16, 64, wl=varlen_workload(cfg, [4000, 2600, 1300]))
+    cfg = small_config("blk_varlen_chunk", 257, B=2, N=3000, Tq=16, kv_dtype="fp8", n_sparse=1)
+    run_block_parity(cfg, 16, 64, wl=varlen_workload(cfg, [3000, 1900]))
+    cfg = small_config("blk_scattered_chunk", 258, B=1, N=3000, Tq=24, n_sparse=1)
+    wl = make_workload(cfg)
+    rng = np.random.default_rng(cfg.cfg_id)
+    pos = rng.integers(0, cfg.N, size=(cfg.B, cfg.Tq)).astype(np.int32)
+    pos[0, 0], pos[0, 1], pos[0, 2] = 0, cfg.N - 1, 700
+    wl.q_pos = pos
+    run_block_parity(cfg, 16, 64, wl=wl)
