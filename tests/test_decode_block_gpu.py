@@ -104,3 +104,24 @@ def test_decode_block_rejects():
     with pytest.raises(hs2.HS2Error):          # query chunks take the separate calls
         q = torch.zeros((cfg.B, 8, cfg.H, cfg.d), dtype=torch.bfloat16, device="cuda")
         hs2.hs2_decode_block(q, [q], g.k, g.v, torch.zeros((cfg.B, 8), dtype=torch.int32, device="cuda"), g.kv_len)
+
+
+def test_decode_block_varlen():
+    """Sequences of different lengths with NaN past each length: the single launch equals the
+    separate calls bit for bit, and its outputs are finite."""
+    from tests.test_parity_gpu import varlen_workload
+    import token_level_sparse_mqa_amd as hs2
+    for cfg, lengths in ((small_config("db_varlen", 275, B=3, N=4000, Tq=2, n_sparse=2), [4000, 2600, 1300]),
+                         (small_config("db_varlen_fp8", 276, B=2, N=5000, Tq=1, kv_dtype="fp8", n_sparse=2),
+                          [3100, 5000])):
+        _say(f"[decode_block] {cfg.name}")
+        g = HipRun(varlen_workload(cfg, lengths))
+        ws = hs2.decode_block_workspace(cfg.B, cfg.Tq, cfg.H, cfg.d, cfg.N, cfg.k_global, cfg.window,
+                                        hs2.dtype_code(g.k), cfg.n_sparse, g.q.device)
+        ref = _separate(g, cfg)
+        got = _fused(g, cfg, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.isfinite(got[0]).all()
+        assert torch.equal(got[1], ref[1])
+        for l in range(cfg.n_sparse):
+            assert torch.equal(got[2][l], ref[2][l]) and torch.isfinite(got[2][l]).all()
