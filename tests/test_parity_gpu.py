@@ -131,6 +131,9 @@ SMALL = [
     # spread over the whole row (decode rows and a query chunk)
     small_config("near_ties_rows", 223, B=2, N=9000, Tq=1, n_sparse=1, near_ties=0.02),
     small_config("near_ties_chunk", 224, B=1, N=7000, Tq=16, n_sparse=1, near_ties=0.02),
+    # FP8 caches at d = 64 with 16 heads (the FP8 row, chunk, score and sparse kernels' d = 64 forms)
+    small_config("fp8_h16_d64", 225, B=2, N=4000, Tq=2, H=16, d=64, kv_dtype="fp8", n_sparse=1),
+    small_config("chunk_fp8_h16_d64", 226, B=1, N=3000, Tq=20, H=16, d=64, kv_dtype="fp8", n_sparse=1),
 ]
 
 
