@@ -237,10 +237,11 @@ def test_bridge_small_exact():
 
 @pytest.mark.parametrize("T,D,d", [(1, 256, 128), (2, 256, 64), (3, 512, 128), (4, 256, 128), (5, 256, 64),
                                    (8, 2048, 128), (33, 256, 128), (64, 4096, 128), (65, 256, 128),
-                                   (1, 4096, 64), (1, 4160, 128)])
+                                   (1, 4096, 64), (1, 4160, 128), (300, 512, 64), (513, 256, 128)])
 def test_bridge_few_rows_exact(T, D, d):
     """Spans of a few rows (a decoded token's) on the vector-matrix kernel, and the sizes around its
-    limits (T = 65 and D = 4160 take the MFMA tiles): integer operands, so bit-exact."""
+    limits (T = 65 and D = 4160 take the MFMA tiles), plus MFMA spans with a ragged last 256-row tile
+    at d = 64 and 128: integer operands, so bit-exact."""
     import token_level_sparse_mqa_amd as hs2
     import oracle
     from workloads.gen import f32_to_bf16_bits
