@@ -77,8 +77,9 @@ hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
+    // the finish reads the digit from a.digits, written by select_digit_kernel or by the gather
     ProfScope ps("select_finish", s);
-    if (given) select_finish_kernel<true><<<a.R, kFinThreads, 0, s>>>(a);
+    if (a.digits) select_finish_kernel<true><<<a.R, kFinThreads, 0, s>>>(a);
     else select_finish_kernel<false><<<a.R, kFinThreads, 0, s>>>(a);
     return hipGetLastError();
 }

@@ -142,7 +142,8 @@ struct GatherLds {
 };
 
 // GIVEN: the row's digit comes from a.digits (written by select_digit_kernel) instead of a search
-// over the row histogram in every wave.
+// over the row histogram in every wave; otherwise the waves search it and the first segment's
+// workgroup writes it to a.digits for the finish.
 template <bool GIVEN = false>
 __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, int seg, GatherLds& S) {
     constexpr int PER = kSelSeg / 256;
@@ -166,7 +167,14 @@ __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, i
     if (C <= a.k_global) return;
     if (j0 >= C) return;
     const int64_t j1 = j0 + kSelSeg < C ? j0 + kSelSeg : C;
-    if constexpr (!GIVEN) wave_digit_from<kHistBins>(hc, (uint32_t)a.k_global, b1, above1);
+    if constexpr (!GIVEN) {
+        wave_digit_from<kHistBins>(hc, (uint32_t)a.k_global, b1, above1);
+        // the first segment's workgroup records the digit, so the finish needs no search of its own
+        if (seg == 0 && threadIdx.x == 0 && a.digits) {
+            a.digits[2 * (int64_t)r] = b1;
+            a.digits[2 * (int64_t)r + 1] = above1;
+        }
+    }
     // bit u of sm / cm: entry u is a sure pick / a bucket candidate (kept in vector registers, so
     // the sixteen per-entry conditions need no lane masks across the reservation below)
     const int nvalid = (int)(j1 - j0);
