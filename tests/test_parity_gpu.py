@@ -462,3 +462,31 @@ def test_scattered_positions(cfg):
     pos[0, 2] = 700                             # fewer candidates than k
     wl.q_pos = pos
     run_parity(cfg, wl=wl)
+
+
+def test_two_streams_concurrently():
+    """A decode workload and a query chunk (full layer, selection and a sparse layer, each call with
+    its own workspace) on two streams at once equal the same calls run one after another: the
+    entry points share no state between calls."""
+    import token_level_sparse_mqa_amd as hs2
+    cfgs = [small_config("streams_decode", 280, B=2, N=6000, Tq=1, n_sparse=1),
+            small_config("streams_chunk", 281, B=1, N=9000, Tq=16, n_sparse=1)]
+    runs = [HipRun(make_workload(c)) for c in cfgs]
+
+    def step(g, cfg):
+        o, idx = hs2.hs2_full_attn_select(g.q, g.k, g.v, g.q_pos, g.kv_len, k_global=cfg.k_global,
+                                          window=cfg.window, sm_scale=g.sm)
+        return o, idx, g.sparse(0, idx)
+
+    ref = [step(g, c) for g, c in zip(runs, cfgs)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        outs = []
+        for g, c, s in zip(runs, cfgs, streams):
+            with torch.cuda.stream(s):
+                outs.append(step(g, c))
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            for x, y in zip(got, want):
+                assert torch.equal(x, y), f"repeat {rep}: a concurrent call differs from the sequential one"
