@@ -438,6 +438,16 @@ def test_sparse_list_semantics(kv, S):
                 assert err <= tol, f"ws={ws} row {(b, i)}: error {err:.3e} > {tol}"
                 if keep.shape[0] == 0:
                     assert np.all(o[b, i] == 0.0)
+    # kv_len omitted (NULL): every entry below Nmax counts, also those past the sequence's length
+    import token_level_sparse_mqa_amd as hs2
+    o = hs2.hs2_sparse_attn(g.qs[0], g.k, g.v, idx_dev, kv_len=None, k_scale=g.k_scale, v_scale=g.v_scale,
+                            sm_scale=g.sm).cpu().numpy()
+    for b in range(cfg.B):
+        for i in range(cfg.Tq):
+            row = idx[b, i].astype(np.int64)
+            ref = O.sparse_row(0, b, i, row[(row >= 0) & (row < cfg.N)])
+            err = float(np.max(np.abs(o[b, i] - ref)))
+            assert err <= tol, f"kv_len=None row {(b, i)}: error {err:.3e} > {tol}"
     _say(f"[sparse-lists] {cfg.name} ok")
 
 
