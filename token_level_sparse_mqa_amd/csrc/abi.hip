@@ -388,7 +388,7 @@ namespace {
 hs2_status full_layer(const SelectPlan& p, const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
                       const float* k_scale, const float* v_scale, const int32_t* q_pos, const int32_t* kv_len,
                       int B, int Tq, int H, int d, int64_t Nmax, int window, float sm_scale, float* o, char* ws,
-                      hipStream_t stream) {
+                      hipStream_t stream, float* bscore = nullptr, int64_t bstride = 0) {
     float* lse = (float*)(ws + p.off_lse);
     float* scores = (float*)(ws + p.off_scores);
     uint32_t* rowhist = (uint32_t*)(ws + p.off_hist);
@@ -422,7 +422,8 @@ hs2_status full_layer(const SelectPlan& p, const void* q, int q_dtype, const voi
     sa.q = q; sa.q_dtype = q_dtype; sa.k = k; sa.kv_dtype = kv_dtype; sa.k_scale = k_scale;
     sa.q_pos = q_pos; sa.kv_len = kv_len; sa.B = B; sa.Tq = Tq; sa.H = H; sa.d = d; sa.Nmax = Nmax;
     sa.window = window; sa.scale_log2 = scale_log2; sa.lse = lse; sa.scores = scores; sa.cstride = Nmax;
-    sa.nsplit = p.score_nsplit; sa.chunk = p.score_chunk; sa.rowhist = rowhist;
+    sa.nsplit = p.score_nsplit; sa.chunk = p.score_chunk; sa.rowhist = bscore ? nullptr : rowhist;
+    sa.bscore = bscore; sa.bstride = bstride;
     e = p.path == PATH_GENERIC ? launch_score_generic(sa, stream)
         : p.path == PATH_MFMA_PREFILL ? launch_score_prefill(sa, stream) : launch_score_rows_mfma(sa, stream);
     if (e != hipSuccess) return hip_fail(e, "score launch");
@@ -561,14 +562,19 @@ hs2_status hs2_full_attn_select_blocks(const void* q, hs2_dtype q_dtype, const v
     if (!workspace || workspace_bytes < need)
         return fail(HS2_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
     char* ws = (char*)workspace;
+    float* bscore = (float*)(ws + p.total);
+    const int64_t bstride = (Nmax + block - 1) / block;
+    // query chunks with blocks of 64 keys (one score-pass stage): the score pass writes the block
+    // maxima itself, unless the token scores are asked for
+    const bool stage_blocks = block == 64 && p.path == PATH_MFMA_PREFILL && !scores_dbg;
     st = full_layer(p, q, q_dtype, k, v, kv_dtype, k_scale, v_scale, q_pos, kv_len, B, Tq, H, d, Nmax, window,
-                    sm_scale, o, ws, stream);
+                    sm_scale, o, ws, stream, stage_blocks ? bscore : nullptr, bstride);
     if (st != HS2_OK) return st;
     SelectArgs se = select_args(p, ws, q_pos, kv_len, Tq, Nmax, K, window, idx, scores_dbg);
     se.block = block; se.k_blocks = k_blocks;
-    se.bscore = (float*)(ws + p.total); se.bstride = (Nmax + block - 1) / block;
+    se.bscore = bscore; se.bstride = bstride;
     se.block_idx = block_idx;
-    hipError_t e = launch_select_blocks(se, stream);
+    hipError_t e = launch_select_blocks(se, stage_blocks, stream);
     if (e != hipSuccess) return hip_fail(e, "block select launch");
     return HS2_OK;
 }

@@ -536,6 +536,19 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     }
 }
 
+// Maximum over the 64 lanes of a wave, in vector registers only: row rotations and quad
+// permutations (DPP) within each 16-lane row, then the 16- and 32-lane swaps across rows.
+__device__ __forceinline__ float pf_wave_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true)));  // row_ror:8
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true)));  // row_ror:4
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // ---- pass 2: selection scores ---------------------------------------------------------------------
 // 64-key stages (two 32-key sub-tiles) in three LDS buffers, software-pipelined per wave: the
 // MFMAs of stage m + 1 are issued before the exponentials of stage m, so the matrix cores and
@@ -663,7 +676,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
                 // both lane halves hold both sums: lane (n, hb) stores key n of sub-tile hb
                 const float v = hb ? acc[1] : acc[0];
                 const int64_t j = (int64_t)m * SK + hb * kTileRows + n;
-                if (j < C) {
+                if (a.bscore) {
+                    // block selection with 64-key blocks: lane l holds key 64 m + l, so the stage's
+                    // block maximum is the wave's (scores are >= 0; -1 marks a key past C)
+                    const float bm = pf_wave_max(j < C ? v : -1.0f);
+                    if (lane == 0) a.bscore[(int64_t)r * a.bstride + m] = bm;
+                } else if (j < C) {
                     srow[j] = v;
                     atomicAdd(&hist[w][__float_as_uint(v) >> 21], 1u);
                 }

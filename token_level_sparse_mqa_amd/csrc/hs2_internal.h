@@ -65,6 +65,10 @@ struct ScoreArgs {
     float* scores; int64_t cstride;      // [R, cstride]
     int nsplit; int64_t chunk;
     uint32_t* rowhist;                   // [R, kHistBins] or nullptr
+    // block-level selection with blocks of one 64-key stage (query-chunk score pass only): the
+    // maximum of each stage's scores goes to bscore [R, bstride] instead of the token scores and
+    // the histogram (nullptr: token scores)
+    float* bscore; int64_t bstride;
 };
 
 struct SelectArgs {
@@ -114,7 +118,7 @@ hipError_t launch_attn_generic(const AttnArgs& a, const char* name, hipStream_t 
 hipError_t launch_attn_combine(const AttnArgs& a, const char* name, hipStream_t s);
 hipError_t launch_score_generic(const ScoreArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s);
-hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t s);
+hipError_t launch_select_blocks(const SelectArgs& a, bool maxima_done, hipStream_t s);
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s);
 bool bridge_rows_fits(const BridgeArgs& a);
 hipError_t launch_bridge_rows(const BridgeArgs& a, hipStream_t s);

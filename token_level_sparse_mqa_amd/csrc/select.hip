@@ -228,8 +228,9 @@ __global__ __launch_bounds__(kBsThreads) void block_select_kernel(SelectArgs a) 
     }
 }
 
-hipError_t launch_select_blocks(const SelectArgs& a, hipStream_t s) {
-    {
+// maxima_done: the score pass already wrote the block maxima (64-key blocks of query chunks)
+hipError_t launch_select_blocks(const SelectArgs& a, bool maxima_done, hipStream_t s) {
+    if (!maxima_done) {
         ProfScope ps("select_block_max", s);
         dim3 grid(a.R, (unsigned)((a.Nmax + kBmSeg - 1) / kBmSeg));
         block_max_kernel<<<grid, 256, 0, s>>>(a);
