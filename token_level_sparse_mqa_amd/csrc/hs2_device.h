@@ -66,23 +66,70 @@ __device__ __forceinline__ int64_t cand_count(int64_t t, int window) {
 
 // ---- wave / block primitives ---------------------------------------------------------------
 
-__device__ __forceinline__ float wave_max(float x) {
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-    return x;
+// Cross-lane steps stay in vector registers (DPP lane moves and the 16- and 32-lane swaps) rather
+// than going through LDS permutes, whose round trips would chain up in these reductions and scans.
+// DPP control words: row_shr:n = 0x110 + n, row_ror:n = 0x120 + n, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143, quad_perm = four 2-bit lane selectors.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    // lanes without a source (or outside ROWS) read 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROWS, 0xF, false);
 }
-__device__ __forceinline__ float wave_sum(float x) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-    return x;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+// a, b: the values of lanes l and l ^ 16 (l ^ 32), in an order that depends on the lane; callers
+// combine them symmetrically (max, or a sum, whose two operands commute exactly)
+__device__ __forceinline__ void lane_pair16(float x, float& a, float& b) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void lane_pair32(float x, float& a, float& b) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Maximum / sum over the 64 lanes (every lane receives the maximum; the sum's rounding order
+// can differ between lanes, so callers take it from one lane).  Within a 16-lane row a rotation by 8,
+// one by 4 and two quad permutations combine all 16 lanes; the swaps then combine the rows.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_f32<0x128>(x));
+    x = fmaxf(x, dpp_f32<0x124>(x));
+    x = fmaxf(x, dpp_f32<0x4E>(x));
+    x = fmaxf(x, dpp_f32<0xB1>(x));
+    float a, b;
+    lane_pair16(x, a, b);
+    lane_pair32(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f32<0x128>(x);
+    x += dpp_f32<0x124>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0xB1>(x);
+    float a, b;
+    lane_pair16(x, a, b);
+    lane_pair32(a + b, a, b);
+    return a + b;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 scan each 16-lane
+// row, then the last lane of row 0 (row 2) is added to row 1 (row 3) and lane 31 to rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
-    const int lane = threadIdx.x & 63;
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    x += dpp_u32<0x111>(x);
+    x += dpp_u32<0x112>(x);
+    x += dpp_u32<0x114>(x);
+    x += dpp_u32<0x118>(x);
+    x += dpp_u32<0x142, 0xA>(x);
+    x += dpp_u32<0x143, 0xC>(x);
     return x;
+}
+// A lane's value broadcast to the wave (lane is wave-uniform).
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
 }
 
 // Exclusive block-wide prefix sum; `tmp` holds NT/64 + 1 words of LDS.  Returns the

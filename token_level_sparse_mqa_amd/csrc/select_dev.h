@@ -56,13 +56,8 @@ __device__ __forceinline__ void wave_digit_from(const uint32_t (&c)[NBINS / 64],
     uint32_t local = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) local += c[i];
-    uint32_t incl = local;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-    }
-    const uint32_t total = __shfl(incl, 63);
+    const uint32_t incl = wave_incl_scan(local);
+    const uint32_t total = lane_value(incl, 63);
     uint32_t run = incl - local;        // entries with a digit above this lane's digits
     int found = -1;
     uint32_t fab = 0;
@@ -74,11 +69,11 @@ __device__ __forceinline__ void wave_digit_from(const uint32_t (&c)[NBINS / 64],
     const uint64_t m = __ballot(found >= 0);
     if (m) {
         const int src = __ffsll((unsigned long long)m) - 1;
-        digit = (uint32_t)__shfl(found, src);
-        above = __shfl(fab, src);
+        digit = lane_value((uint32_t)found, src);
+        above = lane_value(fab, src);
     } else {
         digit = 0;
-        above = total - __shfl(c[0], 63);    // lane 63 holds digits PER-1 .. 0
+        above = total - lane_value(c[0], 63);    // lane 63 holds digits PER-1 .. 0
     }
 }
 
@@ -125,7 +120,7 @@ __device__ __forceinline__ uint32_t wave_append(uint32_t* counter, bool pred) {
     const int leader = __ffsll((unsigned long long)m) - 1;
     uint32_t base = 0;
     if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-    base = __shfl(base, leader);
+    base = lane_value(base, leader);
     return base + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
 }
 
@@ -189,12 +184,7 @@ __device__ __forceinline__ void select_gather_body(const SelectArgs& a, int r, i
     const uint32_t ns = (uint32_t)__popc(sm), nc = (uint32_t)__popc(cm);
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const uint32_t mine = (ns << 16) | nc;
-    uint32_t incl = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(incl, o);
-        if (lane >= o) incl += v;
-    }
+    const uint32_t incl = wave_incl_scan(mine);
     if (lane == 63) S.wtot[w] = incl;
     __syncthreads();
     if (threadIdx.x == 0) {
