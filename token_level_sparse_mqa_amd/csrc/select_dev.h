@@ -461,7 +461,7 @@ __device__ __forceinline__ void select_finish_body(const SelectArgs& a, int r, F
         const uint64_t m = __ballot(pred);
         if (!m) return;
         const int lead = __ffsll((unsigned long long)m) - 1;
-        const uint32_t lb = __shfl(bin, lead);
+        const uint32_t lb = lane_value(bin, lead);
         if (__ballot(pred && bin != lb) == 0) {
             if ((int)(threadIdx.x & 63) == lead) atomicAdd(&hist[lb], (uint32_t)__popcll(m));
         } else if (pred) {
