@@ -116,6 +116,21 @@ __device__ __forceinline__ float wave_sum(float x) {
     return a + b;
 }
 
+// Maximum over aligned groups of `group` lanes (a power of two up to 64, wave-uniform): each lane
+// receives its group's maximum.  Quad permutations pair lanes 1 and 2 apart, the half-row and row
+// mirrors (0x141, 0x140) pair the 4-lane quads and the 8-lane halves of a 16-lane row, and the swaps
+// pair the rows.
+__device__ __forceinline__ float group_max(float x, int group) {
+    if (group >= 2) x = fmaxf(x, dpp_f32<0xB1>(x));
+    if (group >= 4) x = fmaxf(x, dpp_f32<0x4E>(x));
+    if (group >= 8) x = fmaxf(x, dpp_f32<0x141>(x));
+    if (group >= 16) x = fmaxf(x, dpp_f32<0x140>(x));
+    float a, b;
+    if (group >= 32) { lane_pair16(x, a, b); x = fmaxf(a, b); }
+    if (group >= 64) { lane_pair32(x, a, b); x = fmaxf(a, b); }
+    return x;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 scan each 16-lane
 // row, then the last lane of row 0 (row 2) is added to row 1 (row 3) and lane 31 to rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
