@@ -131,11 +131,9 @@ __device__ __forceinline__ void score_rows_body(const ScoreArgs& a, int bx, int 
                     float acc = 0.f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) acc += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], sc, nlse[i]));
-                    {
-                        float x0, x1;                            // this lane's and the partner's 16 heads
-                        lane_pair32(acc, x0, x1);
-                        acc = x0 + x1;
-                    }
+                    // The partner lane holds the other 16 heads. An LDS permute here, not the 32-lane
+                    // swap: this loop is bound by vector issue, and the permute's latency hides behind it.
+                    acc += __shfl_xor(acc, 32);
                     const int64_t j = e0 + 32 * tile + n;
                     if (hb == 0 && j < e1) {
                         srow[j] = acc;
