@@ -243,8 +243,8 @@ size_t hs2_decode_block_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t
  * (exactly hs2_full_attn_select) followed by L sparse layers on the indices it selected (exactly
  * hs2_sparse_attn_layers with a workspace), as one cooperative kernel launch whose phases are
  * separated by grid-wide barriers (lynxflow "Two-Level KV Sharing": the sparse layers reuse the
- * full layer's cache and indices; ainews page: latency depends on kernel efficiency, data
- * movement and scheduling).
+ * full layer's cache and indices; ainews page, closing paragraph: the compute saving on paper
+ * becomes a wall-clock saving only through the kernels, the memory traffic and the launch order).
  *   q : bf16 [B, Tq, H, d] (the full layer's queries); q_sparse : HOST array of L device pointers
  *   to bf16 [B, Tq, H, d]; o : fp32 [B, Tq, H, d]; idx : int32 [B, Tq, k_global + window];
  *   o_sparse : HOST array of L device pointers to fp32 [B, Tq, H, d].  Everything else as for

@@ -2,8 +2,8 @@
 // merge of the splits (o and the per-head log-sum-exp), the selection scores, the top-k
 // selection with the window, and every sparse layer of the block over the selected rows with its
 // own merge (lynxflow blog, "Two-Level KV Sharing": the sparse layers reuse the full layer's cache
-// and indices; ainews page: end-to-end latency hinges on kernel efficiency, data movement and
-// scheduling).
+// and indices; ainews page, closing paragraph: the compute saving on paper becomes a wall-clock
+// saving only through the kernels, the memory traffic and the launch order).
 //
 // A cooperative launch of exactly as many workgroups as fit on the GPU at once (the runtime
 // refuses a launch that cannot be resident).  Each phase is a list of work items (the workgroups

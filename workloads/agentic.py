@@ -4,7 +4,7 @@ The pages build the hybrid block around agentic inference: each round the agent 
 action, the environment answers with a long observation that has to be prefilled, and the one
 context keeps growing (agentik-os article, "How HySparse2 shrinks agent KV and prefill": section 1
 "Agentic inference as the driving workload", and the same article's "How it fits into an agentic
-stack": every observation is appended to one long context buffer).  The
+stack": the agent's single context grows by each observation in turn).  The
 pages give no lengths; the configs below pick a short action of a few dozen tokens and an
 observation of one 4,096-token chunk, starting from a context that already holds a long trace.
 
