@@ -12,8 +12,8 @@
  *                         the 1,024 best-scoring earlier positions one by one plus a forced window
  *                         of the 128 most recent positions (kucoin news flash; lynxflow blog,
  *                         "Token-Level Sparse Selection"; agentik-os article, section 3).
- *   hs2_sparse_attn       A sparse layer of the same hybrid block: it reuses the full layer's KV
- *                         cache and selection indices (KV Reuse: lynxflow "Two-Level KV Sharing";
+ *   hs2_sparse_attn       A sparse layer of the same hybrid block: it reads the full layer's K/V
+ *                         rows and picked positions as they are (KV Reuse: lynxflow "Two-Level KV Sharing";
  *                         agentik-os section 2) and attends over only the selected rows.
  *
  * The pages leave the selection score open (agentik-os, "What is not documented").  This

@@ -1,11 +1,10 @@
 """Seeded inputs of the agentic multi-turn workload (no arithmetic of the method lives here).
 
-The pages build the hybrid block around agentic inference: each round the agent emits a short
-action, the environment answers with a long observation that has to be prefilled, and the one
-context keeps growing (agentik-os article, "How HySparse2 shrinks agent KV and prefill": section 1
-"Agentic inference as the driving workload", and the same article's "How it fits into an agentic
-stack": the agent's single context grows by each observation in turn).  The
-pages give no lengths; the configs below pick a short action of a few dozen tokens and an
+The pages build the hybrid block around agentic inference: in every round a few decoded action
+tokens are followed by a long observation to prefill, on top of a context that only gets longer
+(agentik-os article, "How HySparse2 shrinks agent KV and prefill": section 1 "Agentic inference as
+the driving workload", and the same article's "How it fits into an agentic stack": the agent's
+single context grows by each observation in turn).  The pages give no lengths; the configs below pick a short action of a few dozen tokens and an
 observation of one 4,096-token chunk, starting from a context that already holds a long trace.
 
 One sequence (one agent trace).  Positions 0 .. N0-1 are the trace already in the cache; then
