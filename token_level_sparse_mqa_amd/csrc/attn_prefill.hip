@@ -658,7 +658,12 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
         mma(sa, 0);
         // iteration m: the scores of stage m and the MFMAs of stage m + 1 in one branch-free block
         // (MFMAs past the last stage read a stale buffer and their results go unused), then the
-        // stores of stage m's scores, stage m + 2 into LDS and the loads of stage m + 4
+        // stores of stage m's scores, stage m + 2 into LDS and the loads of stage m + 4.
+        // Iterations come in pairs that always run both halves, and the LDS store of stage m + 2 is
+        // unconditional (past the last stage the clamped loads hold the last stage again, written
+        // into a buffer no later MFMA of a live stage reads): the loop then has one back edge with
+        // one set of loads in flight, and the compiler's wait before that store covers only the
+        // loads of stage m + 2, not those of stage m + 3 issued one iteration later.
         auto iter = [&](int m, f32x16_t* cur, f32x16_t* nxt) {
             float acc[SUB];
             scores(cur, m % NBUF, acc);
@@ -686,13 +691,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
                     atomicAdd(&hist[w][__float_as_uint(v) >> 21], 1u);
                 }
             }
-            if (m + 2 < nstages) store(m + 2);
+            store(m + 2);
             load(m + 4);
             __syncthreads();
         };
         for (int m = 0; m < nstages; m += 2) {
             iter(m, sa, sb);
-            if (m + 1 < nstages) iter(m + 1, sb, sa);
+            iter(m + 1, sb, sa);
         }
     }
     // this workgroup owns its rows' histograms entirely
