@@ -119,46 +119,55 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
     store(0, 0);
     __syncthreads();
     const int g = lane >> 4, q = lane & 15;
-    for (int base = 0; base < nk; base += NST) {
+    // chunk kc from LDS buffer kc & 1, then register slot u + 1 into the other buffer and the loads
+    // of chunk kc + NST into slot u
+    auto step = [&](int kc, int u, bool store_next) {
+        const int buf = kc & 1;
+        const char* hb_ = hs[buf];
+        const char* wb_ = ws[buf];
 #pragma unroll
-        for (int u = 0; u < NST; ++u) {
-            const int kc = base + u;
-            if (kc >= nk) break;
-            const int buf = kc & 1;
-            const char* hb_ = hs[buf];
-            const char* wb_ = ws[buf];
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            // A: hidden rows 64 wm + 32 i + n, d = 16 ks + 8 hb + {0..7}
+            bf16x8_t aop[G::MB];
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                // A: hidden rows 64 wm + 32 i + n, d = 16 ks + 8 hb + {0..7}
-                bf16x8_t aop[G::MB];
+            for (int i = 0; i < G::MB; ++i)
+                aop[i] = *(const bf16x8_t*)(hb_ + G::hoff(64 * wm + 32 * i + n, 2 * ks + hb));
+#pragma unroll
+            for (int j = 0; j < G::NB; ++j) {
+                // B: weight rows d = 16 ks + 8 hb + 4 h + (q >> 2), columns wn*d + 32 j + 16 (g & 1) + 4 (q & 3)
+                const int col = DD * wn + 32 * j + 16 * (g & 1) + 4 * (q & 3);
+                u32x4_t r;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int krow = 16 * ks + 8 * (g >> 1) + 4 * h + (q >> 2);
+                    const char* p = wb_ + G::woff(krow, col >> 3) + (col & 7) * 2;
+                    const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
+                    const u32x2_t tu = __builtin_bit_cast(u32x2_t, t);
+                    r[2 * h] = tu[0];
+                    r[2 * h + 1] = tu[1];
+                }
+                const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, r);
 #pragma unroll
                 for (int i = 0; i < G::MB; ++i)
-                    aop[i] = *(const bf16x8_t*)(hb_ + G::hoff(64 * wm + 32 * i + n, 2 * ks + hb));
-#pragma unroll
-                for (int j = 0; j < G::NB; ++j) {
-                    // B: weight rows d = 16 ks + 8 hb + 4 h + (q >> 2), columns wn*d + 32 j + 16 (g & 1) + 4 (q & 3)
-                    const int col = DD * wn + 32 * j + 16 * (g & 1) + 4 * (q & 3);
-                    u32x4_t r;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int krow = 16 * ks + 8 * (g >> 1) + 4 * h + (q >> 2);
-                        const char* p = wb_ + G::woff(krow, col >> 3) + (col & 7) * 2;
-                        const v4i16_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)p);
-                        const u32x2_t tu = __builtin_bit_cast(u32x2_t, t);
-                        r[2 * h] = tu[0];
-                        r[2 * h + 1] = tu[1];
-                    }
-                    const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, r);
-#pragma unroll
-                    for (int i = 0; i < G::MB; ++i)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop, acc[i][j], 0, 0, 0);
-                }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop, acc[i][j], 0, 0, 0);
             }
-            if (kc + 1 < nk) store((u + 1) % NST, buf ^ 1);
-            load(u, kc + NST);
-            __syncthreads();
         }
+        if (store_next) store((u + 1) % NST, buf ^ 1);
+        load(u, kc + NST);
+        __syncthreads();
+    };
+    // Whole groups of NST chunks run without a branch: the store of the chunk after the last one
+    // writes clamped loads into a buffer nothing reads any more.  A conditional store or an early
+    // exit inside the group gives the loop several back edges with different loads in flight,
+    // and the compiler's wait analysis then stalls each group on loads issued just before it.
+    int kc = 0;
+    for (; kc + NST <= nk; kc += NST) {
+#pragma unroll
+        for (int u = 0; u < NST; ++u) step(kc + u, u, true);
     }
+#pragma unroll
+    for (int u = 0; u < NST - 1; ++u)
+        if (kc + u < nk) step(kc + u, u, kc + u + 1 < nk);
 
     // epilogue: bf16 (round to nearest even); wave column half 0 writes K, half 1 writes V
     uint16_t* out = wn == 0 ? a.k_out : a.v_out;
