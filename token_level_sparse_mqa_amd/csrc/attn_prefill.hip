@@ -551,14 +551,19 @@ __device__ __forceinline__ float pf_wave_max(float x) {
 
 // ---- pass 2: selection scores ---------------------------------------------------------------------
 // 64-key stages (two 32-key sub-tiles) in three LDS buffers, software-pipelined per wave: the
-// MFMAs of stage m + 1 are issued before the exponentials of stage m, so the matrix cores and
+// MFMAs of stage m + 1 are interleaved with the exponentials of stage m, so the matrix cores and
 // the vector ALUs of a wave work at the same time.  One barrier per stage.
+constexpr int kScoreAhead = 4;               // LDS operand reads in flight ahead of the MFMAs
 template <int D, int KV>
 __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs a) {
     constexpr int KS = D / 16;
     constexpr int NX = PfGeom<D, KV, kPfThreads>::NX;
     constexpr int SUB = 2, SK = SUB * kTileRows, NBUF = 3;
-    __shared__ __attribute__((aligned(16))) char kt[NBUF][SUB][LdsTile<D>::BYTES];
+    // K rows padded to PfTiles<D>::KST bytes, as in the attention pass: every operand read of a
+    // stage is one base address plus an immediate offset (a swizzled tile needs an address
+    // computation per read)
+    using TL = PfTiles<D>;
+    __shared__ __attribute__((aligned(16))) char kt[NBUF][SUB][TL::KB];
     __shared__ float ks_s[NBUF][SUB][kTileRows];
     __shared__ uint32_t hist[kPfWaves][kHistBins];
     __shared__ int64_t t_s[kPfWaves];
@@ -617,7 +622,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
             const int buf = stage % NBUF, rs = stage & 1;
 #pragma unroll
             for (int sub = 0; sub < SUB; ++sub) {
-                pf_store_k<D, KV, kPfThreads, 0>(rk[rs][sub], kt[buf][sub], threadIdx.x);
+                pf_store_k<D, KV, kPfThreads, TL::KST>(rk[rs][sub], kt[buf][sub], threadIdx.x);
                 if (KV == HS2_FP8_E4M3 && threadIdx.x < kTileRows) ks_s[buf][sub][threadIdx.x] = rks[rs][sub];
             }
         };
@@ -628,23 +633,11 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
                 sacc[sub] = f32x16_t{};
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
-                    sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[s], lds_row_operand<D>(kt[buf][sub], n, hb * (D / 16) + s),
-                                                                        sacc[sub], 0, 0, 0);
+                    sacc[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        qop[s], *(const bf16x8_t*)(kt[buf][sub] + n * TL::KST + (hb * (D / 16) + s) * 16), sacc[sub], 0, 0, 0);
             }
         };
-        // score(j) = sum_h 2^(x_h(j) - lse_h): 16 heads per lane, the partner lane's 16 through
-        // v_permlane32_swap
-        auto scores = [&](const f32x16_t* sacc, int buf, float* acc) {
-#pragma unroll
-            for (int sub = 0; sub < SUB; ++sub) {
-                float sc = a.scale_log2;
-                if (KV == HS2_FP8_E4M3) sc *= ks_s[buf][sub][n];
-                float x = 0.f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) x += __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][i], sc, nlse[i]));
-                acc[sub] = pf_half_sum(x);
-            }
-        };
+        const int klane = n * TL::KST + hb * (D / 16) * 16;   // this lane's operand row and half
         f32x16_t sa[SUB], sb[SUB];            // S of consecutive stages (even / odd)
         load(0);
         store(0);
@@ -665,18 +658,52 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
         // one set of loads in flight, and the compiler's wait before that store covers only the
         // loads of stage m + 2, not those of stage m + 3 issued one iteration later.
         auto iter = [&](int m, f32x16_t* cur, f32x16_t* nxt) {
-            float acc[SUB];
-            scores(cur, m % NBUF, acc);
-            mma(nxt, (m + 1) % NBUF);
-            // MFMA k-steps interleaved with the exponentials: LDS operand reads run two k-steps
-            // ahead, about six vector instructions between MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            // One static sequence of SUB * KS steps.  Step i issues MFMA i of stage m + 1 (k-step
+            // i / SUB of sub-tile i % SUB, so consecutive MFMAs use different accumulators), the LDS
+            // read of the operand kScoreAhead steps later, and EPS of the lane's 32 exponentials of
+            // stage m (sub-tile v / 16, head slot v % 16 for v = EPS i .. EPS i + EPS - 1; EPS = 2
+            // at d = 128, 4 at d = 64).  A scheduling barrier
+            // closes every step: without it the compiler issued all MFMAs, each behind its own
+            // operand read, and then all exponentials, so a wave's MFMAs and vector work did not
+            // overlap.  Each sum keeps its order (head slots 0..15), so results do not change.
+            constexpr int NM = SUB * KS;
+            constexpr int EPS = SUB * 16 / NM;       // exponentials per step
+            static_assert(EPS * NM == SUB * 16, "every exponential belongs to one step");
+            const int mb = (m + 1) % NBUF;
+            float sc[SUB];
 #pragma unroll
-            for (int i = 0; i < SUB * KS; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (i + 2 < SUB * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+            for (int sub = 0; sub < SUB; ++sub) {
+                sc[sub] = a.scale_log2;
+                if (KV == HS2_FP8_E4M3) sc[sub] *= ks_s[m % NBUF][sub][n];
             }
+            // one scalar buffer offset plus the lane's fixed offset; the reads differ by immediates
+            const int boff = __builtin_amdgcn_readfirstlane(mb * (SUB * TL::KB));
+            const char* kbase = &kt[0][0][0] + boff + klane;
+            auto rd = [&](int i) { return *(const bf16x8_t*)(kbase + (i % SUB) * TL::KB + (i / SUB) * 16); };
+            bf16x8_t win[kScoreAhead];
+#pragma unroll
+            for (int i = 0; i < kScoreAhead; ++i) win[i] = rd(i);
+            float x[SUB] = {0.f, 0.f};
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) nxt[sub] = f32x16_t{};
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < NM; ++i) {
+                const bf16x8_t op = win[i % kScoreAhead];
+                if (i + kScoreAhead < NM) win[i % kScoreAhead] = rd(i + kScoreAhead);
+                nxt[i % SUB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qop[i / SUB], op, nxt[i % SUB], 0, 0, 0);
+#pragma unroll
+                for (int u = 0; u < EPS; ++u) {
+                    const int v = EPS * i + u, vs = v / 16, e = v % 16;
+                    x[vs] += __builtin_amdgcn_exp2f(__builtin_fmaf(cur[vs][e], sc[vs], nlse[e]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            // score(j) = sum_h 2^(x_h(j) - lse_h): 16 heads per lane, the partner lane's 16
+            // through v_permlane32_swap
+            float acc[SUB];
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) acc[sub] = pf_half_sum(x[sub]);
             if (m <= last) {
                 // both lane halves hold both sums: lane (n, hb) stores key n of sub-tile hb
                 const float v = hb ? acc[1] : acc[0];
