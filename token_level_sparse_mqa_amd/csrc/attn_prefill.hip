@@ -536,17 +536,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     }
 }
 
-// Maximum over the 64 lanes of a wave, in vector registers only: row rotations and quad
-// permutations (DPP) within each 16-lane row, then the 16- and 32-lane swaps across rows.
-__device__ __forceinline__ float pf_wave_max(float x) {
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, true)));  // row_ror:8
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x124, 0xF, 0xF, true)));  // row_ror:4
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true)));   // quad [2,3,0,1]
-    x = fmaxf(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true)));   // quad [1,0,3,2]
-    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-    const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+// Maximum over the 64 lanes of a wave of values that are >= 0 or negative markers that are all
+// equal, in vector registers only: row rotations and quad permutations (DPP) within each 16-lane
+// row, then the 16- and 32-lane swaps across rows.  For such values the signed integer order of
+// the bit patterns is the float order, so one integer max per step does the work (a float max
+// costs three here: the compiler canonicalises both operands first).
+__device__ __forceinline__ float pf_wave_max_nonneg(float v) {
+    int x = __float_as_int(v);
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true));   // row_ror:8
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x124, 0xF, 0xF, true));   // row_ror:4
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true));    // quad [2,3,0,1]
+    x = max(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true));    // quad [1,0,3,2]
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+    x = max((int)p[0], (int)p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+    return __int_as_float(max((int)q[0], (int)q[1]));
 }
 
 // ---- pass 2: selection scores ---------------------------------------------------------------------
@@ -711,7 +715,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
                 if (a.bscore) {
                     // block selection with 64-key blocks: lane l holds key 64 m + l, so the stage's
                     // block maximum is the wave's (scores are >= 0; -1 marks a key past C)
-                    const float bm = pf_wave_max(j < C ? v : -1.0f);
+                    const float bm = pf_wave_max_nonneg(j < C ? v : -1.0f);
                     if (lane == 0) a.bscore[(int64_t)r * a.bstride + m] = bm;
                 } else if (j < C) {
                     srow[j] = v;

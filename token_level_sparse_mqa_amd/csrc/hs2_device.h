@@ -116,19 +116,27 @@ __device__ __forceinline__ float wave_sum(float x) {
     return a + b;
 }
 
-// Maximum over aligned groups of `group` lanes (a power of two up to 64, wave-uniform): each lane
-// receives its group's maximum.  Quad permutations pair lanes 1 and 2 apart, the half-row and row
-// mirrors (0x141, 0x140) pair the 4-lane quads and the 8-lane halves of a 16-lane row, and the swaps
-// pair the rows.
-__device__ __forceinline__ float group_max(float x, int group) {
-    if (group >= 2) x = fmaxf(x, dpp_f32<0xB1>(x));
-    if (group >= 4) x = fmaxf(x, dpp_f32<0x4E>(x));
-    if (group >= 8) x = fmaxf(x, dpp_f32<0x141>(x));
-    if (group >= 16) x = fmaxf(x, dpp_f32<0x140>(x));
-    float a, b;
-    if (group >= 32) { lane_pair16(x, a, b); x = fmaxf(a, b); }
-    if (group >= 64) { lane_pair32(x, a, b); x = fmaxf(a, b); }
-    return x;
+// Maximum over aligned groups of `group` lanes (a power of two up to 64, wave-uniform) of values
+// that are >= 0 or negative markers that are all equal: each lane receives its group's maximum.
+// Quad permutations pair lanes 1 and 2 apart, the half-row and row mirrors (0x141, 0x140) pair the
+// 4-lane quads and the 8-lane halves of a 16-lane row, and the swaps pair the rows.  For such
+// values the signed integer order of the bit patterns is the float order, so each step is one
+// integer max (a float max costs three: the compiler canonicalises both operands first).
+__device__ __forceinline__ float group_max_nonneg(float v, int group) {
+    int x = __float_as_int(v);
+    if (group >= 2) x = max(x, (int)dpp_u32<0xB1>((uint32_t)x));
+    if (group >= 4) x = max(x, (int)dpp_u32<0x4E>((uint32_t)x));
+    if (group >= 8) x = max(x, (int)dpp_u32<0x141>((uint32_t)x));
+    if (group >= 16) x = max(x, (int)dpp_u32<0x140>((uint32_t)x));
+    if (group >= 32) {
+        const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+        x = max((int)p[0], (int)p[1]);
+    }
+    if (group >= 64) {
+        const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+        x = max((int)p[0], (int)p[1]);
+    }
+    return __int_as_float(x);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 scan each 16-lane

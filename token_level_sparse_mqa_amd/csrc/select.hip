@@ -94,7 +94,7 @@ hipError_t launch_select(const SelectArgs& a, bool hist_done, hipStream_t s) {
 
 // Block maxima of one 4096-position segment of a row: thread x of the workgroup reads positions
 // j0 + x + 256u, so a wave covers 64 consecutive positions per load and the `block` lanes of a
-// block (block divides 64) fold their maximum in vector registers (group_max).
+// block (block divides 64) fold their maximum in vector registers (group_max_nonneg).
 constexpr int kBmSeg = 4096;
 
 __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a) {
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void block_max_kernel(SelectArgs a) {
         v[u] = j < C ? sc[j] : -1.0f;            // scores are >= 0; -1 marks a position past C
     }
 #pragma unroll
-    for (int u = 0; u < PER; ++u) v[u] = group_max(v[u], a.block);
+    for (int u = 0; u < PER; ++u) v[u] = group_max_nonneg(v[u], a.block);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
         const int64_t j = j0 + u * 256 + threadIdx.x;
