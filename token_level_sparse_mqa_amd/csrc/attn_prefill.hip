@@ -463,18 +463,19 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                     // weights 2^(x - mr) into the fp16 P operand (times the V row scale for FP8);
                     // returns the lane's fp32 sum of the unscaled weights (l feeds the log-sum-exp
                     // of the selection scores, which needs more than fp16 precision)
+                    // (four partial sums, so that the adds do not form one dependent chain of 32)
                     auto weights = [&](float mr) -> float {
-                        float ps = 0.f;
+                        float ps4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int sub = 0; sub < SUB; ++sub)
 #pragma unroll
                             for (int i = 0; i < 16; ++i) {
                                 float e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[sub][i], scl, -mr));
-                                ps += e2;
+                                ps4[i & 3] += e2;
                                 if (KV == HS2_FP8_E4M3) e2 *= vs_s[kb][sub][8 * (i >> 2) + 4 * hb + (i & 3)];
                                 p[sub][i >> 3][i & 7] = (_Float16)e2;
                             }
-                        return ps;
+                        return (ps4[0] + ps4[1]) + (ps4[2] + ps4[3]);
                     };
                     // the reference stays while every lane's weights sum to at most kPfWeightMax;
                     // otherwise (and on the wave's first stage) it moves to the running maximum
