@@ -84,11 +84,11 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
         p.score_chunk = p.chunk;
     } else {
         const int64_t min_chunk = kv_dtype == HS2_FP8_E4M3 ? 2048 : 512;
-        // attention: about four workgroups per CU over the pass; score pass: about two (one
+        // attention: about three workgroups per CU over the pass; score pass: about two (one
         // wave of workgroups, so no workgroup's start-up latency falls into the stream).
         // Both were chosen by measurement on the decode workloads.  The minimum chunk only binds
-        // for a few rows (one sequence at 128K keys: 257 workgroups instead of 129).
-        split_range(p.R, Nmax, 1024, min_chunk, 128, &p.nsplit, &p.chunk);
+        // for a few rows (one sequence at 128K keys: 256 workgroups instead of 768).
+        split_range(p.R, Nmax, 768, min_chunk, 128, &p.nsplit, &p.chunk);
         split_range(p.R, Nmax, 512, min_chunk, 128, &p.score_nsplit, &p.score_chunk);
     }
     p.nseg = (int)ceil_div(Nmax, kSelSeg);
