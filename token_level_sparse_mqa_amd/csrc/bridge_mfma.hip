@@ -7,12 +7,15 @@
 // bound by HBM: one pass over the hidden states, the weights served from L2.
 //
 // A workgroup owns 256 token rows and all 2d output columns (K and V together, so the hidden
-// states are read once): eight waves in a 4 x 2 grid, each with 64 rows x d columns of fp32
-// accumulators (2 x 4 MFMA blocks at d = 128, which keeps the LDS operand reads per MFMA low).
-// The reduction over D runs in chunks of 64: the hidden-state chunk [256 x 64] and the weight
-// chunk [64 x 2d] are staged in LDS (double-buffered), with the global loads of the next
-// chunks in flight in registers.  A operands are hidden-state rows (8 consecutive d per lane);
-// B operands come from the row-major weight chunk through ds_read_b64_tr_b16.
+// states are read once): eight waves in a 2 x 4 grid at d = 128, each with 128 rows x 64 columns
+// of fp32 accumulators (4 x 2 MFMA blocks: per 16 reduction steps a wave reads 4 hidden operands
+// at the full LDS rate and 2 weight operands through the half-rate transposed reads, 20% fewer
+// LDS cycles than 2 x 4 blocks), 2 x 4 waves of 128 x 32 at d = 64.  The reduction over D runs
+// in chunks of 64.  Hidden-state chunks [256 x 64] (three LDS buffers) and weight chunks [64 x 2d]
+// (two at d = 128, three at d = 64) go from memory straight into LDS, so no registers hold loads
+// in flight and two hidden chunks stream in while one is multiplied.  A operands are hidden-state
+// rows (8 consecutive d per lane); B operands come from the row-major weight chunk through
+// ds_read_b64_tr_b16.
 #include "mfma_tiles.h"
 
 namespace hs2 {
@@ -20,13 +23,10 @@ namespace hs2 {
 constexpr int kBrM = 256;          // token rows per workgroup
 constexpr int kBrThreads = 512;    // eight waves
 constexpr int kBrK = 64;           // reduction chunk
-constexpr int kBrStages = 2;       // chunks in flight in registers (deeper pipelines measured slower)
 
 template <int DD, int BK>   // output columns per projection, reduction chunk
 struct BrGeom {
     static constexpr int N = 2 * DD;                 // K and V columns
-    static constexpr int MB = 2;                     // MFMA row blocks per wave (64 rows)
-    static constexpr int NB = DD / 32;               // MFMA column blocks per wave (d columns)
     static constexpr int HROW = BK * 2;              // bytes per hidden-state row in LDS
     static constexpr int HCPR = BK / 8;              // 16-byte chunks per hidden row
     static constexpr int HRPB = 256 / HROW;          // hidden rows per 256-byte bank cycle
@@ -34,10 +34,6 @@ struct BrGeom {
     static constexpr int WCPR = N / 8;               // 16-byte chunks per weight row
     static constexpr int HBYTES = kBrM * HROW;
     static constexpr int WBYTES = BK * WROW;
-    static constexpr int HCH = kBrM * HCPR;          // 16-byte chunks of a hidden chunk
-    static constexpr int WCH = BK * WCPR;            // 16-byte chunks of a weight chunk
-    static constexpr int HX = HCH / kBrThreads;
-    static constexpr int WX = (WCH + kBrThreads - 1) / kBrThreads;
     // An operand read covers 16 hidden rows (16 lanes, one chunk each), HRPB rows to a bank cycle:
     // chunk XOR ((row / HRPB) mod HCPR) gives them 16 different bank groups.
     __device__ static __forceinline__ int hoff(int row, int chunk) {
@@ -51,91 +47,142 @@ struct BrGeom {
     }
 };
 
-// BK-deep reduction chunks, NST of them in flight in registers: a chunk's loads are issued
-// NST - 1 chunks before it is stored to LDS, so NST - 1 chunk computations hide their latency.
-template <int DD, int BK, int NST>
+// The reduction chunk that workgroup blockIdx.x takes at step kc.  If every workgroup walked the
+// chunks in the same order, the 256 resident workgroups would all read the same 64- or 128-byte
+// column slice of their 4 KB hidden rows (and the same weight rows) at once, which concentrates the
+// requests on a few memory channels; starting each workgroup's walk 5 chunks after the previous
+// workgroup's spreads them (measured on the prefill-exit shape: the loads alone 337 -> 269 us).
+// The sum over the chunks is then taken in a rotated order, a different fp32 rounding order per
+// workgroup; integer-valued operands stay exact.
+__device__ __forceinline__ int stagger_chunk(int kc, int nk) {
+    return (int)(((uint32_t)kc + blockIdx.x * 5u) % (uint32_t)nk);
+}
+
+// Loads into LDS: global_load_lds_dwordx4 writes lane i's 16 bytes at bytes [16 i, 16 i + 16) of a
+// 1 KB block whose base is wave-uniform.  A block's lanes fetch the global chunks that belong at
+// their LDS slots under the XOR swizzles above, so the operand reads see the swizzled layout.
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// One wave-wide load of 16 bytes per lane into LDS bytes [lds, lds + 1024) (lds wave-uniform),
+// lane i's bytes at lds + 16 i: from `base + off` (uniform base, per-lane 32-bit offset), or from a
+// per-lane address.  Written as inline asm so that the compiler does not take every later LDS read
+// for a possible reader of these bytes and wait for all loads before it: the kernel orders them
+// itself (s_waitcnt vmcnt, then a workgroup barrier, before a stage is read).  The instruction has
+// no register results; its address registers are read when it issues.  M0 (the LDS base) is saved
+// and restored around it, since the compiler does not track M0 through inline asm.
+__device__ __forceinline__ void dma16(const char* base, uint32_t off, uint32_t lds) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(off), "s"(base), "s"(lds) : "memory");
+}
+__device__ __forceinline__ void dma16(const char* addr, uint32_t lds) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(addr), "s"(lds) : "memory");
+}
+
+// s_waitcnt with only vmcnt = N (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Hidden-state chunks take NSH LDS buffers and weight chunks NSW (NSH or NSH - 1: the weights come
+// from L2 with a shorter latency); the loads of chunk kc + NSH - 1 (hidden) and kc + NSW - 1
+// (weights) are issued while chunk kc is multiplied, weights first.
+template <int DD, int BK, int NSH, int NSW, int MB>
 __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a) {
     using G = BrGeom<DD, BK>;
-    __shared__ __attribute__((aligned(16))) char hs[2][G::HBYTES];
-    __shared__ __attribute__((aligned(16))) char ws[2][G::WBYTES];
+    // waves in a WR x WC grid, each with MB x NB MFMA blocks of 32 x 32
+    constexpr int WR = kBrM / (32 * MB), WC = 8 / WR, NB = (2 * DD / 32) / WC;
+    static_assert(WR * WC == 8 && NB * WC * 32 == 2 * DD, "wave grid");
+    static_assert(NSW == NSH || NSW == NSH - 1, "weight buffers: NSH or NSH - 1");
+    static_assert(NSW >= 2, "at least double buffering");
+    constexpr int HBLK = G::HBYTES / 8192;                // 1 KB hidden blocks per wave and chunk
+    constexpr int WBLK = G::WBYTES / 8192;                // 1 KB weight blocks per wave and chunk
+    static_assert(G::HBYTES % 8192 == 0 && G::WBYTES % 8192 == 0, "chunk blocks per wave");
+    // loads (per lane) issued after the later of a chunk's hidden and weight loads, once the loads of
+    // the chunk NSH - 2 steps ahead are out: what may stay in flight when that chunk is needed
+    constexpr int AFTER = NSW == NSH ? (NSH - 2) * (HBLK + WBLK) : HBLK + (NSH - 3) * (HBLK + WBLK);
+    __shared__ __attribute__((aligned(1024))) char smem[NSH * G::HBYTES + NSW * G::WBYTES];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int n = lane & 31, hb = lane >> 5;
-    const int wm = w >> 1, wn = w & 1;                 // wave rows [64 wm, +64), columns [d wn, +d)
+    const int wm = w / WC, wn = w % WC;
     const int64_t m0 = (int64_t)blockIdx.x * kBrM;
     const int nk = a.D / BK;
 
-    // per-thread load slots: 32-bit byte offsets from the workgroup's first hidden row / weights
+    // per-lane source of each block this wave fills: the logical chunk that the swizzle places at
+    // the lane's LDS slot (32-bit byte offsets from the workgroup's first hidden row; weight addresses)
     const char* hbase = (const char*)(a.hidden + m0 * a.D);
-    uint32_t hoffs[G::HX];
-    int hst[G::HX];
+    uint32_t hsrc[HBLK];
 #pragma unroll
-    for (int x = 0; x < G::HX; ++x) {
-        const int q = tid + x * kBrThreads;
-        const int row = q / G::HCPR, c = q % G::HCPR;
+    for (int x = 0; x < HBLK; ++x) {
+        const int o = (w + 8 * x) * 1024 + 16 * lane;
+        const int row = o / G::HROW, p = (o % G::HROW) >> 4;
+        const int c = p ^ ((row / G::HRPB) & (G::HCPR - 1));
         const int64_t gr = m0 + row < a.T ? row : a.T - 1 - m0;
-        hoffs[x] = (uint32_t)(gr * a.D * 2 + 16 * c);
-        hst[x] = G::hoff(row, c);
+        hsrc[x] = (uint32_t)(gr * a.D * 2 + 16 * c);
     }
-    uint32_t woffs[G::WX];
-    int wst[G::WX];
-    bool wisk[G::WX];
+    const char* wsrc[WBLK];
 #pragma unroll
-    for (int x = 0; x < G::WX; ++x) {
-        int q = tid + x * kBrThreads;
-        q = q < G::WCH ? q : G::WCH - 1;
-        const int kr = q / G::WCPR, c = q % G::WCPR;      // c < WCPR/2: Wk, else Wv
-        wisk[x] = c < G::WCPR / 2;
-        const int cc = wisk[x] ? c : c - G::WCPR / 2;
-        woffs[x] = (uint32_t)(kr * DD * 2 + 16 * cc);
-        wst[x] = G::woff(kr, c);
+    for (int x = 0; x < WBLK; ++x) {
+        const int o = (w + 8 * x) * 1024 + 16 * lane;
+        const int kr = o / G::WROW, p = (o % G::WROW) >> 4;
+        const int c = p ^ (((kr & 3) << 2) | (((kr >> 2) & 1) << 1));
+        const bool isk = c < G::WCPR / 2;
+        const int cc = isk ? c : c - G::WCPR / 2;
+        wsrc[x] = (const char*)(isk ? a.wk : a.wv) + (kr * DD * 2 + 16 * cc);
     }
-    u32x4_t rh[NST][G::HX], rw[NST][G::WX];
-    auto load = [&](int st, int kc) {
-        kc = kc < nk ? kc : nk - 1;
-        const uint32_t hk = (uint32_t)kc * BK * 2;                 // bytes along a hidden row
-        const uint32_t wk = (uint32_t)kc * BK * DD * 2;            // bytes down the weights
+    // chunk kc (clamped: loads issued past the end re-read the last chunk into a buffer that nothing
+    // reads any more), taken in the workgroup's rotated order
+    const uint32_t lds_h = (uint32_t)(size_t)(lds_char_t*)smem + __builtin_amdgcn_readfirstlane(w) * 1024;
+    const uint32_t lds_w = lds_h + NSH * G::HBYTES;
+    auto issue_h = [&](int kc) {
+        const uint32_t sb = lds_h + (kc % NSH) * G::HBYTES;
+        kc = stagger_chunk(kc < nk ? kc : nk - 1, nk);
 #pragma unroll
-        for (int x = 0; x < G::HX; ++x) rh[st][x] = ld16<false>(hbase + (hoffs[x] + hk));
-#pragma unroll
-        for (int x = 0; x < G::WX; ++x)
-            rw[st][x] = *(const u32x4_t*)((const char*)(wisk[x] ? a.wk : a.wv) + (woffs[x] + wk));
+        for (int x = 0; x < HBLK; ++x) dma16(hbase, hsrc[x] + (uint32_t)kc * BK * 2, sb + 8192 * x);
     };
-    auto store = [&](int st, int buf) {
+    auto issue_w = [&](int kc) {
+        const uint32_t sb = lds_w + (kc % NSW) * G::WBYTES;
+        kc = stagger_chunk(kc < nk ? kc : nk - 1, nk);
 #pragma unroll
-        for (int x = 0; x < G::HX; ++x) *(u32x4_t*)(hs[buf] + hst[x]) = rh[st][x];
-#pragma unroll
-        for (int x = 0; x < G::WX; ++x)
-            if (tid + x * kBrThreads < G::WCH) *(u32x4_t*)(ws[buf] + wst[x]) = rw[st][x];
+        for (int x = 0; x < WBLK; ++x) dma16(wsrc[x] + (uint32_t)kc * BK * DD * 2, sb + 8192 * x);
     };
 
-    f32x16_t acc[G::MB][G::NB];
+    f32x16_t acc[MB][NB];
 #pragma unroll
-    for (int i = 0; i < G::MB; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < G::NB; ++j) acc[i][j] = f32x16_t{};
+        for (int j = 0; j < NB; ++j) acc[i][j] = f32x16_t{};
 
+    // the steady-state issue order (weights of chunk j + NSW - 1, then hidden of chunk j + NSH - 1)
+    // run for j = 1 - NSH .. -1, skipping chunks below 0
 #pragma unroll
-    for (int u = 0; u < NST; ++u) load(u, u);
-    store(0, 0);
-    __syncthreads();
+    for (int j = 1 - NSH; j < 0; ++j) {
+        if (j + NSW - 1 >= 0) issue_w(j + NSW - 1);
+        issue_h(j + NSH - 1);
+    }
     const int g = lane >> 4, q = lane & 15;
-    // chunk kc from LDS buffer kc & 1, then register slot u + 1 into the other buffer and the loads
-    // of chunk kc + NST into slot u
-    auto step = [&](int kc, int u, bool store_next) {
-        const int buf = kc & 1;
-        const char* hb_ = hs[buf];
-        const char* wb_ = ws[buf];
+    for (int kc = 0; kc < nk; ++kc) {
+        // this wave's loads of chunk kc have landed once at most AFTER loads are outstanding; the
+        // barrier then covers every wave's, and every wave is done with chunk kc - 1's buffers
+        wait_vmcnt<AFTER>();
+        __syncthreads();
+        issue_w(kc + NSW - 1);
+        issue_h(kc + NSH - 1);
+        const char* hb_ = smem + (kc % NSH) * G::HBYTES;
+        const char* wb_ = smem + NSH * G::HBYTES + (kc % NSW) * G::WBYTES;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            // A: hidden rows 64 wm + 32 i + n, d = 16 ks + 8 hb + {0..7}
-            bf16x8_t aop[G::MB];
+            bf16x8_t aop[MB];
 #pragma unroll
-            for (int i = 0; i < G::MB; ++i)
-                aop[i] = *(const bf16x8_t*)(hb_ + G::hoff(64 * wm + 32 * i + n, 2 * ks + hb));
+            for (int i = 0; i < MB; ++i)
+                aop[i] = *(const bf16x8_t*)(hb_ + G::hoff(32 * MB * wm + 32 * i + n, 2 * ks + hb));
 #pragma unroll
-            for (int j = 0; j < G::NB; ++j) {
-                // B: weight rows d = 16 ks + 8 hb + 4 h + (q >> 2), columns wn*d + 32 j + 16 (g & 1) + 4 (q & 3)
-                const int col = DD * wn + 32 * j + 16 * (g & 1) + 4 * (q & 3);
+            for (int j = 0; j < NB; ++j) {
+                const int col = 32 * NB * wn + 32 * j + 16 * (g & 1) + 4 * (q & 3);
                 u32x4_t r;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
@@ -148,47 +195,35 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
                 }
                 const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, r);
 #pragma unroll
-                for (int i = 0; i < G::MB; ++i)
+                for (int i = 0; i < MB; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop, acc[i][j], 0, 0, 0);
             }
         }
-        if (store_next) store((u + 1) % NST, buf ^ 1);
-        load(u, kc + NST);
-        __syncthreads();
-    };
-    // Whole groups of NST chunks run without a branch: the store of the chunk after the last one
-    // writes clamped loads into a buffer nothing reads any more.  A conditional store or an early
-    // exit inside the group gives the loop several back edges with different loads in flight,
-    // and the compiler's wait analysis then stalls each group on loads issued just before it.
-    int kc = 0;
-    for (; kc + NST <= nk; kc += NST) {
-#pragma unroll
-        for (int u = 0; u < NST; ++u) step(kc + u, u, true);
     }
-#pragma unroll
-    for (int u = 0; u < NST - 1; ++u)
-        if (kc + u < nk) step(kc + u, u, kc + u + 1 < nk);
+    wait_vmcnt<0>();      // the clamped loads past the end land before the workgroup ends
 
-    // epilogue: bf16 (round to nearest even); wave column half 0 writes K, half 1 writes V
-    uint16_t* out = wn == 0 ? a.k_out : a.v_out;
+    // epilogue: bf16 (round to nearest even); columns below d are K's, the rest V's
 #pragma unroll
-    for (int i = 0; i < G::MB; ++i)
+    for (int j = 0; j < NB; ++j) {
+        const int c = 32 * NB * wn + 32 * j;                     // wave-uniform block column
+        uint16_t* out = c < DD ? a.k_out : a.v_out;
+        const int oc = (c < DD ? c : c - DD) + n;
 #pragma unroll
-        for (int j = 0; j < G::NB; ++j) {
-            const int oc = 32 * j + n;
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * hb + (e & 3);
+                const int64_t row = m0 + 32 * MB * wm + 32 * i + 8 * (e >> 2) + 4 * hb + (e & 3);
                 if (row < a.T) out[row * a.stride + oc] = f32_to_bf16_rne(acc[i][j][e]);
             }
-        }
+    }
 }
 
 hipError_t launch_bridge_mfma(const BridgeArgs& a, hipStream_t s) {
     ProfScope ps("bridge_mfma", s);
     dim3 grid((unsigned)((a.T + kBrM - 1) / kBrM));
-    if (a.d == 128) bridge_mfma_kernel<128, kBrK, kBrStages><<<grid, kBrThreads, 0, s>>>(a);
-    else bridge_mfma_kernel<64, kBrK, kBrStages><<<grid, kBrThreads, 0, s>>>(a);
+    // 160 KB of LDS at d = 128 (3 hidden + 2 weight buffers of 32 KB), 144 KB at d = 64 (3 + 3)
+    if (a.d == 128) bridge_mfma_kernel<128, kBrK, 3, 2, 4><<<grid, kBrThreads, 0, s>>>(a);
+    else bridge_mfma_kernel<64, kBrK, 3, 3, 4><<<grid, kBrThreads, 0, s>>>(a);
     return hipGetLastError();
 }
 
