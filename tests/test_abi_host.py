@@ -292,15 +292,19 @@ def _need(fn, **kw):
 @pytest.mark.parametrize("kvd,row_bytes", [(hs2.HS2_BF16, 256), (hs2.HS2_FP8_E4M3, 128)])
 def test_long_chunk_takes_row_kernels(kvd, row_bytes):
     """Query chunks whose cache spans more than 2^31 bytes per sequence leave the chunk kernels
-    (32-bit offsets) for the row kernels, whose key splits show up in the call's own workspace
-    plan as partial results: 8 rows x 96 splits x 32 heads x (d + 2) floats (about 768
-    workgroups over the 8 rows)."""
+    (32-bit offsets) for the row kernels.  The chunk kernels' plan holds the sequence's V^T
+    images (d rows of 80 bytes per 32 keys, whole 64-key stages); the row kernels' plan drops
+    them and adds their key splits' partial results: 8 rows x 96 splits x 32 heads x (d + 2)
+    floats (about 768 workgroups over the 8 rows)."""
     fit = (1 << 31) // row_bytes - 1                 # the largest cache the chunk kernels take
     ks = vs = FAKE if kvd == hs2.HS2_FP8_E4M3 else None
     a = _need(_fas, Tq=8, N=fit, kvd=kvd, ks=ks, vs=vs)
     b = _need(_fas, Tq=8, N=fit + 128, kvd=kvd, ks=ks, vs=vs)
     scores_growth = 8 * 128 * 4
-    assert b - a >= scores_growth + 8 * 96 * 32 * 130 * 4
+    vt_images = 2 * ((fit + 63) // 64) * 128 * 80
+    assert a > vt_images
+    assert b - a >= scores_growth + 8 * 96 * 32 * 130 * 4 - vt_images
+    assert b - a <= scores_growth + 8 * 96 * 32 * 130 * 4 - vt_images + (1 << 12)
     # decode rows take the row kernels at every length: no jump there
     c = _need(_fas, Tq=4, N=fit, kvd=kvd, ks=ks, vs=vs)
     e = _need(_fas, Tq=4, N=fit + 128, kvd=kvd, ks=ks, vs=vs)

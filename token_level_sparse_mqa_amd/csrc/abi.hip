@@ -54,7 +54,8 @@ struct SelectPlan {
     int nsplit; int64_t chunk;         // attention pass over keys
     int score_nsplit; int64_t score_chunk;
     int nseg;
-    size_t off_part, off_lse, off_scores, off_hist, off_cnt, off_sure, off_cand, off_digits, total;
+    size_t off_part, off_lse, off_scores, off_hist, off_cnt, off_sure, off_cand, off_digits, off_vt, total;
+    int64_t vt_nsub;                    // query chunks: V^T images per sequence (whole 64-key stages)
 };
 
 // Split a key range of n entries over workgroups: at least `min_chunk` entries each (a multiple
@@ -101,6 +102,9 @@ SelectPlan plan_select(int B, int Tq, int H, int d, int64_t Nmax, int k_global, 
     p.off_cand = off;   off = align_up(off + (size_t)p.R * kSelCap * 8);
     p.off_scores = off; off = align_up(off + (size_t)p.R * Nmax * 4);
     p.off_digits = off; off = align_up(off + (size_t)p.R * 2 * 4);
+    // query chunks: every sequence's V as fp16 V^T images of 32-key sub-tiles, d rows of 80 bytes
+    p.vt_nsub = p.path == PATH_MFMA_PREFILL ? 2 * ceil_div(Nmax, 64) : 0;
+    p.off_vt = off;     off = align_up(off + (size_t)B * p.vt_nsub * d * 80);
     p.total = off;
     return p;
 }
@@ -405,6 +409,7 @@ hs2_status full_layer(const SelectPlan& p, const void* q, int q_dtype, const voi
     aa.part_ml = aa.part ? aa.part + p.R * p.nsplit * H * d : nullptr;   // MFMA layout
     aa.o = o; aa.lse = lse;
     aa.zero_hist = rowhist; aa.zero_cnt = counters;     // cleared by the attention pass
+    aa.vt_img = ws + p.off_vt; aa.vt_nsub = p.vt_nsub;
     if (p.path == PATH_GENERIC) {
         e = launch_attn_generic(aa, "full_attn_generic", stream);
         if (e != hipSuccess) return hip_fail(e, "attention launch");

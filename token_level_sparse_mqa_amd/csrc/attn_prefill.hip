@@ -106,45 +106,6 @@ __device__ __forceinline__ void pf_store_k(const u32x4_t* raw, char* lds, int ti
     }
 }
 
-__device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
-// fp16 LDS tile from raw V, rows at a stride of ST bytes.  The conversion truncates (round toward
-// zero).  A bf16 value has 8 significant bits, so it is exact in fp16 for |v| in [2^-17, 65504]
-// (down to the fp16 subnormal step 2^-24); smaller magnitudes lose less than 2^-24, larger ones
-// clamp to 65504.  FP8 E4M3 codes (magnitudes 2^-9 .. 448) convert exactly.
-template <int D, int KV, int NT, int ST>
-__device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds, int tid) {
-    using G = RawGeom<D, KV>;
-    using P = PfGeom<D, KV, NT>;
-#pragma unroll
-    for (int x = 0; x < P::NX; ++x) {
-        const int q = tid + x * NT;
-        if (q >= P::CHUNKS) continue;
-        const int R = q / G::CPR, c = q % G::CPR;
-        if (KV == HS2_FP8_E4M3) {
-            u32x4_t lo, hi;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const f32x2_t a = fp8x2_to_f32<false>(raw[x][w]), b = fp8x2_to_f32<true>(raw[x][w]);
-                const uint32_t p0 = f16x2_bits(a[0], a[1]), p1 = f16x2_bits(b[0], b[1]);
-                if (w < 2) { lo[2 * w] = p0; lo[2 * w + 1] = p1; } else { hi[2 * w - 4] = p0; hi[2 * w - 3] = p1; }
-            }
-            *(u32x4_t*)(lds + R * ST + 32 * c) = lo;
-            *(u32x4_t*)(lds + R * ST + 32 * c + 16) = hi;
-        } else {
-            u32x4_t o;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t u = raw[x][w];
-                o[w] = f16x2_bits(__uint_as_float(u << 16), __uint_as_float(u & 0xffff0000u));
-            }
-            *(u32x4_t*)(lds + R * ST + 16 * c) = o;
-        }
-    }
-}
-
 // LDS tiles of the attention pass, rows padded instead of swizzled so that every operand read of
 // a stage is one base address plus an immediate offset.
 //   K:   key rows, stride 2D + 16 bytes (8 consecutive rows of a b128 read start 4 banks apart).
@@ -152,12 +113,59 @@ __device__ __forceinline__ void pf_store_v(const u32x4_t* raw, char* lds, int ti
 //        b128 read cover disjoint banks).  Keys are stored in the order the P operand uses:
 //        within each 16-key step, positions 8 hb + j hold key 8 (j / 4) + 4 hb + j % 4, so a
 //        lane's 8 operand values are one 16-byte chunk.
-//   V staging: key rows, stride 2D + 64 bytes, read once with transposing reads to build V^T.
+//   The V^T tiles come ready-made from vt_prep_kernel, which writes every 32-key sub-tile of the
+//   cache once per call as this LDS image (pad bytes included), so a workgroup copies them in
+//   whole 16-byte chunks: no conversion, no transposing reads, no scattered writes per workgroup.
+//   (Rows of 64 bytes with the chunks XOR-swizzled instead of padded, 20% fewer bytes to copy,
+//   measured 11% slower: the operand reads lose their common base address.)
 template <int D>
 struct PfTiles {
-    static constexpr int KST = 2 * D + 16, VTST = 80, VST = 2 * D + 64;
-    static constexpr int KB = kTileRows * KST, VTB = D * VTST, VB = kTileRows * VST;
+    static constexpr int KST = 2 * D + 16, VTST = 80;
+    static constexpr int KB = kTileRows * KST, VTB = D * VTST;
+    static constexpr int VTCH = VTB / 16;        // 16-byte chunks of a V^T image
 };
+
+// ---- V^T images -----------------------------------------------------------------------------------
+// Sub-tile st (keys 32 st .. 32 st + 31) of sequence b becomes D rows of 80 bytes: row n holds dim n
+// of the 32 keys as fp16, in the order the P operand uses (16-byte chunk c = 2 ks + hb holds keys
+// 16 ks + 4 hb + {0..3} and 16 ks + 8 + 4 hb + {0..3}), then 16 pad bytes.  Keys at or past the
+// sequence's length read its last key (finite data that the softmax weights by zero).  The
+// conversion truncates (round toward zero): a bf16 value has 8 significant bits, so it is exact in
+// fp16 for |v| in [2^-17, 65504] (down to the fp16 subnormal step 2^-24); smaller magnitudes lose
+// less than 2^-24, larger ones clamp to 65504.  FP8 E4M3 codes (magnitudes 2^-9 .. 448) convert
+// exactly; their row scales stay with P.
+__device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
+template <int D, int KV>
+__global__ __launch_bounds__(256) void vt_prep_kernel(AttnArgs a) {
+    using TL = PfTiles<D>;
+    const int b = blockIdx.y;
+    const int64_t st = blockIdx.x;
+    const int64_t L = seq_len(a.kv_len, b, a.Nmax);
+    const int64_t last = L > 0 ? L - 1 : 0;
+    const int64_t rowbase = (int64_t)b * a.Nmax;
+    char* img = a.vt_img + ((int64_t)b * a.vt_nsub + st) * TL::VTB;
+    for (int q = threadIdx.x; q < TL::VTCH; q += 256) {
+        const int c = q / D, n = q % D;            // consecutive threads: consecutive dims of one chunk
+        u32x4_t o = u32x4_t{};
+        if (c < 4) {
+            const int ks = c >> 1, hb = c & 1;
+            float f[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                int64_t key = st * kTileRows + 16 * ks + 8 * (j >> 2) + 4 * hb + (j & 3);
+                key = key < last ? key : last;
+                f[j] = load_elem(a.v, a.kv_dtype == HS2_FP8_E4M3 ? HS2_FP8_E4M3 : HS2_BF16, (rowbase + key) * D + n);
+            }
+#pragma unroll
+            for (int w = 0; w < 4; ++w) o[w] = f16x2_bits(f[2 * w], f[2 * w + 1]);
+        }
+        *(u32x4_t*)(img + n * TL::VTST + 16 * c) = o;
+    }
+}
+
 
 // Positions of the workgroup's query rows; returns the largest one (or -1).
 __device__ __forceinline__ int64_t pf_rows(const int32_t* q_pos, const int32_t* kv_len, int Tq, int64_t Nmax,
@@ -188,19 +196,20 @@ __device__ __forceinline__ float pf_half_sum(float x) {
 // Two wave groups of four waves share each SIMD pairwise and run half a stage apart: while one
 // group multiplies (P.V of the previous stage, then S of the current one) the other runs the
 // online softmax of its last S, so the matrix cores and the vector ALUs work at the same time.
-// A workgroup barrier closes every half-stage.  Group g loads, stages and transposes sub-tile g
-// of every stage.
+// A workgroup barrier closes every half-stage.  Group g loads and stages sub-tile g of every
+// stage (its K rows and its ready-made V^T image).
 //
 // Half-step h, group g, e = h - g:
 //   e = 2m:    O += P(m-1).V(m-1) and S(m) = K(m).Q as one software-pipelined MFMA sequence
 //              (LDS operands read a few MFMAs ahead); in its middle the group stores its K rows
-//              and staged V rows of stage m+1 and issues the loads of stage m+2.  The wave runs
-//              at raised priority so that its MFMAs are not starved by the other group's VALU.
-//   e = 2m+1:  transposing reads of the staged V rows of stage m+1, then P(m) = softmax step on
-//              S(m), then the V^T writes of stage m+1.
+//              of stage m+1 and issues the loads of stage m+2's K rows and stage m+1's V^T
+//              image.  The wave runs at raised priority so that its MFMAs are not starved by the
+//              other group's VALU.
+//   e = 2m+1:  P(m) = softmax step on S(m), then the V^T image writes of stage m+1.
 // Three LDS stage buffers cover a stage's lifetime (K is read during the two halves of its own
-// stage, V^T during the next two).  V^T costs one transposing read per element per workgroup;
-// reading V transposed in every wave would cost eight, at half the rate of b128 reads.
+// stage, V^T during the next two).  Building V^T inside the workgroup (convert, stage, transposing
+// reads, writes) took about 10% of the kernel's time in the softmax half; the images are built
+// once per call instead (vt_prep_kernel).
 //
 // The softmax keeps a lazy reference point per head: the weights 2^(x - ref) of a stage are
 // computed against the stored reference and kept if every lane's 32 weights sum to at most
@@ -226,7 +235,6 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     using TL = PfTiles<D>;
     __shared__ __attribute__((aligned(16))) char kt[NBUF][SUB][TL::KB];
     __shared__ __attribute__((aligned(16))) char vt[NBUF][SUB][TL::VTB];
-    __shared__ __attribute__((aligned(16))) char vstage[SUB][TL::VB];
     __shared__ float ks_s[NBUF][SUB][kTileRows], vs_s[NBUF][SUB][kTileRows];
     __shared__ int64_t t_s[kPfWaves];
 
@@ -263,16 +271,18 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
     if (nstages > 0) {
         const int64_t khi = tmax + 1;
         const char* kseq = (const char*)a.k + rowbase * RawGeom<D, KV>::RB;
-        const char* vseq = (const char*)a.v + rowbase * RawGeom<D, KV>::RB;
         const PfLoader<D, KV, NT> ld(gtid);
-        u32x4_t rk[NX], rv[NX];
+        u32x4_t rk[NX];
+        // this group's V^T image of a stage: 16-byte chunks gtid + NT x (the last ones clamped)
+        constexpr int NXV = (TL::VTCH + NT - 1) / NT;
+        u32x4_t rvt[NXV];
+        const char* vtseq = a.vt_img + (int64_t)b * a.vt_nsub * TL::VTB;
         float rks = 0.f, rvs = 0.f;
         // this group's sub-tile of a stage, clamped into the key range
         auto load = [&](int stage) {
             const int sg = stage < nstages ? stage : nstages - 1;
             const int64_t k0 = (int64_t)sg * SK + grp * kTileRows;
             ld.load_clamped(rk, kseq, k0, khi);
-            ld.load_clamped(rv, vseq, k0, khi);
             if (KV == HS2_FP8_E4M3) {
                 const int64_t key = k0 + (gtid & 31);
                 const int64_t kc = key < khi ? key : khi - 1;
@@ -280,41 +290,29 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                 rvs = a.v_scale[rowbase + kc];
             }
         };
+        // the V^T image of a stage is loaded in the multiplying half before it and written at the
+        // end of the softmax half before it, where the LDS writes do not lengthen the MFMA half
+        auto load_v = [&](int stage) {
+            const int sg = stage < nstages ? stage : nstages - 1;
+            const char* img = vtseq + (int64_t)(sg * SUB + grp) * TL::VTB;
+#pragma unroll
+            for (int x = 0; x < NXV; ++x) {
+                const int q = gtid + x * NT;
+                rvt[x] = *(const u32x4_t*)(img + 16 * (q < TL::VTCH ? q : TL::VTCH - 1));
+            }
+        };
+        auto store_v = [&](int buf) {
+#pragma unroll
+            for (int x = 0; x < NXV; ++x) {
+                const int q = gtid + x * NT;
+                if (q < TL::VTCH) *(u32x4_t*)(vt[buf][grp] + 16 * q) = rvt[x];
+            }
+        };
         auto store = [&](int buf) {
             pf_store_k<D, KV, NT, TL::KST>(rk, kt[buf][grp], gtid);
-            pf_store_v<D, KV, NT, TL::VST>(rv, vstage[grp], gtid);
             if (KV == HS2_FP8_E4M3 && gtid < kTileRows) {
                 ks_s[buf][grp][gtid] = rks;
                 vs_s[buf][grp][gtid] = rvs;
-            }
-        };
-        // V^T of this group's sub-tile from the staged rows: wave w % 4 builds (dv block, key step)
-        // pairs c = w % 4 + 4 u; the two transposing reads give lane (G, q) dim 32 blk + lane % 32
-        // of keys 16 ks + 4 hb + {0..3} and 16 ks + 8 + 4 hb + {0..3}.  Split into reads and writes
-        // so that the softmax math runs while the reads are in flight.
-        constexpr int NTU = (NB * 2 + 3) / 4;    // pairs per wave
-        auto t_read = [&](u32x4_t* rr) {
-            const int G = lane >> 4, q = lane & 15;
-            const char* src = vstage[grp] + (4 * hb + (q >> 2)) * TL::VST + (16 * (G & 1) + 4 * (q & 3)) * 2;
-#pragma unroll
-            for (int u = 0; u < NTU; ++u) {
-                const int cc = 4 * u + (w & 3);
-                const int blk = (cc < NB * 2 ? cc : 0) >> 1, ks = cc & 1;
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const char* pp = src + (16 * ks + 8 * h2) * TL::VST + blk * 64;
-                    const u32x2_t tu = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)pp));
-                    rr[u][2 * h2] = tu[0];
-                    rr[u][2 * h2 + 1] = tu[1];
-                }
-            }
-        };
-        auto t_write = [&](const u32x4_t* rr, int buf) {
-            char* dst = vt[buf][grp] + n * TL::VTST + 16 * hb;
-#pragma unroll
-            for (int u = 0; u < NTU; ++u) {
-                const int cc = 4 * u + (w & 3);
-                if (cc < NB * 2) *(u32x4_t*)(dst + (cc >> 1) * 32 * TL::VTST + 32 * (cc & 1)) = rr[u];
             }
         };
         f32x16_t sacc[SUB];                      // S of a stage, from its multiply to its softmax
@@ -326,13 +324,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
             p[sub][1] = f16x8_t{};
         }
         load(0);
+        load_v(0);
         store(0);
-        __syncthreads();
-        {
-            u32x4_t tr[NTU];
-            t_read(tr);
-            t_write(tr, 0);
-        }
+        store_v(0);
         load(1);
         __syncthreads();
         for (int h = 0; h < 2 * nstages + 2; ++h) {
@@ -405,6 +399,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                         if (i == MID) {
                             store((m + 1) % NBUF);
                             load(m + 2);
+                            load_v(m + 1);
                         }
                     }
                     // keep the order: the prologue reads, then per item its MFMA followed by the
@@ -433,11 +428,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                 else {
                     store((m + 1) % NBUF);
                     load(m + 2);
+                    load_v(m + 1);
                 }
             } else if (e >= 0) {
-                // ---- softmax half of stage m: first the group's V^T of stage m + 1 ----
-                u32x4_t tr[NTU];
-                if (m + 1 < nstages) t_read(tr);
+                // ---- softmax half of stage m ----
                 if (m < nstages && m <= last) {
                     const int kb = m % NBUF;
                     const int64_t k0 = (int64_t)m * SK;
@@ -507,7 +501,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void attn_prefill_kernel(AttnArgs a)
                     }
                     l_run += ps;
                 }
-                if (m + 1 < nstages) t_write(tr, (m + 1) % NBUF);
+                if (m + 1 < nstages) store_v((m + 1) % NBUF);
             }
             __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
@@ -742,7 +736,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void score_prefill_kernel(ScoreArgs 
     }
 }
 
+// V^T images of every sequence's cache (vt_nsub sub-tiles each), then the attention pass.
 hipError_t launch_attn_prefill(const AttnArgs& a, hipStream_t s) {
+    {
+        ProfScope ps("vt_prep", s);
+        dim3 grid((unsigned)a.vt_nsub, a.B);
+        if (a.kv_dtype == HS2_FP8_E4M3) {
+            if (a.d == 128) vt_prep_kernel<128, HS2_FP8_E4M3><<<grid, 256, 0, s>>>(a);
+            else vt_prep_kernel<64, HS2_FP8_E4M3><<<grid, 256, 0, s>>>(a);
+        } else {
+            if (a.d == 128) vt_prep_kernel<128, HS2_BF16><<<grid, 256, 0, s>>>(a);
+            else vt_prep_kernel<64, HS2_BF16><<<grid, 256, 0, s>>>(a);
+        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     ProfScope ps("full_attn_prefill", s);
     const int nqt = (a.Tq + kPfWaves - 1) / kPfWaves;
     dim3 grid(a.B * nqt);

@@ -53,6 +53,10 @@ struct AttnArgs {
     const void* ql[kMaxLayers];
     float* ol[kMaxLayers];
     int64_t part_lstride, ml_lstride;
+    // Query chunks: V of every sequence as fp16 V^T images of 32-key sub-tiles (the attention
+    // kernel's LDS layout), vt_nsub per sequence, written by vt_prep_kernel before the attention.
+    char* vt_img;
+    int64_t vt_nsub;
 };
 
 struct ScoreArgs {
