@@ -259,6 +259,30 @@ def test_bridge_few_rows_exact(T, D, d):
     assert np.all(oracle.decode(c[:2], "bf16") == -5.0) and np.all(oracle.decode(c[2 + T:], "bf16") == -5.0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bridge_odd_stride_exact(d):
+    """MFMA spans (ragged last tile) into rows whose stride is not a multiple of 4 elements and
+    whose V part starts 2 bytes past an 8-byte boundary, so the kernel's 8-byte row writes are
+    not allowed and it writes element by element: integer operands, bit-exact; the column
+    between K and V and the rows around them stay untouched."""
+    import token_level_sparse_mqa_amd as hs2
+    import oracle
+    from workloads.gen import f32_to_bf16_bits
+    rng = np.random.default_rng(31 + d)
+    T, D = 300, 256
+    hb = f32_to_bf16_bits(rng.integers(-3, 4, size=(T, D)).astype(np.float32))
+    wkb = f32_to_bf16_bits(rng.integers(-3, 4, size=(D, d)).astype(np.float32))
+    wvb = f32_to_bf16_bits(rng.integers(-3, 4, size=(D, d)).astype(np.float32))
+    cache = torch.full((T + 2, 2 * d + 1), -9.0, dtype=torch.bfloat16, device="cuda")
+    hs2.hs2_kv_bridge(to_dev(hb, "bf16"), to_dev(wkb, "bf16"), to_dev(wvb, "bf16"),
+                      k_out=cache[1:1 + T, :d], v_out=cache[1:1 + T, d + 1:], out_row_stride=2 * d + 1)
+    c = bits_from_dev(cache)
+    ko, vo = oracle.kv_bridge(hb, wkb, wvb)
+    assert np.array_equal(c[1:1 + T, :d], ko) and np.array_equal(c[1:1 + T, d + 1:], vo)
+    dec = oracle.decode(c, "bf16")
+    assert np.all(dec[1:1 + T, d] == -9.0) and np.all(dec[0] == -9.0) and np.all(dec[1 + T] == -9.0)
+
+
 def test_bridge_one_row_random():
     """One decoded token at the workload's width: random operands within the fp32 summation bound."""
     import token_level_sparse_mqa_amd as hs2

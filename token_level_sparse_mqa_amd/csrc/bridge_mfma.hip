@@ -94,7 +94,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int DD, int BK, int NSH, int NSW, int MB>
 __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a) {
     using G = BrGeom<DD, BK>;
-    // waves in a WR x WC grid, each with MB x NB MFMA blocks of 32 x 32
+    // waves in a WR x WC grid, each with MB x NB MFMA blocks of 32 x 32 (held transposed)
     constexpr int WR = kBrM / (32 * MB), WC = 8 / WR, NB = (2 * DD / 32) / WC;
     static_assert(WR * WC == 8 && NB * WC * 32 == 2 * DD, "wave grid");
     static_assert(NSW == NSH || NSW == NSH - 1, "weight buffers: NSH or NSH - 1");
@@ -196,25 +196,41 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
                 const bf16x8_t bop = __builtin_bit_cast(bf16x8_t, r);
 #pragma unroll
                 for (int i = 0; i < MB; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[i], bop, acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bop, aop[i], acc[i][j], 0, 0, 0);
             }
         }
     }
     wait_vmcnt<0>();      // the clamped loads past the end land before the workgroup ends
 
-    // epilogue: bf16 (round to nearest even); columns below d are K's, the rest V's
+    // epilogue: bf16 (round to nearest even); columns below d are K's, the rest V's.  The MFMAs
+    // take the weights as their first operand, so block (i, j) holds the transposed product: lane
+    // (n, hb) has token 32 i + n and, for each q, the 4 consecutive output columns 8 q + 4 hb + 0..3
+    // (e = 4 q .. 4 q + 3), stored as one 8-byte write where the rows allow it.
+    const bool st8 = (a.stride & 3) == 0 && ((uintptr_t)a.k_out & 7) == 0 && ((uintptr_t)a.v_out & 7) == 0;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
         const int c = 32 * NB * wn + 32 * j;                     // wave-uniform block column
         uint16_t* out = c < DD ? a.k_out : a.v_out;
-        const int oc = (c < DD ? c : c - DD) + n;
+        const int oc0 = (c < DD ? c : c - DD) + 4 * hb;
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < MB; ++i) {
+            const int64_t row = m0 + 32 * MB * wm + 32 * i + n;
+            if (row >= a.T) continue;
+            uint16_t* orow = out + row * a.stride + oc0;
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + 32 * MB * wm + 32 * i + 8 * (e >> 2) + 4 * hb + (e & 3);
-                if (row < a.T) out[row * a.stride + oc] = f32_to_bf16_rne(acc[i][j][e]);
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * q]) |
+                                    ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16);
+                const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 2]) |
+                                    ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16);
+                if (st8) {
+                    *(u32x2_t*)(orow + 8 * q) = u32x2_t{lo, hi};
+                } else {
+                    orow[8 * q] = (uint16_t)lo; orow[8 * q + 1] = (uint16_t)(lo >> 16);
+                    orow[8 * q + 2] = (uint16_t)hi; orow[8 * q + 3] = (uint16_t)(hi >> 16);
+                }
             }
+        }
     }
 }
 
