@@ -202,34 +202,44 @@ __global__ __launch_bounds__(kBrThreads, 1) void bridge_mfma_kernel(BridgeArgs a
     }
     wait_vmcnt<0>();      // the clamped loads past the end land before the workgroup ends
 
-    // epilogue: bf16 (round to nearest even); columns below d are K's, the rest V's.  The MFMAs
-    // take the weights as their first operand, so block (i, j) holds the transposed product: lane
-    // (n, hb) has token 32 i + n and, for each q, the 4 consecutive output columns 8 q + 4 hb + 0..3
-    // (e = 4 q .. 4 q + 3), stored as one 8-byte write where the rows allow it.
-    const bool st8 = (a.stride & 3) == 0 && ((uintptr_t)a.k_out & 7) == 0 && ((uintptr_t)a.v_out & 7) == 0;
+    // epilogue: bf16 (round to nearest even), staged through LDS so that global rows are written
+    // whole.  The MFMAs take the weights as their first operand, so block (i, j) holds the
+    // transposed product: lane (n, hb) has token 32 i + n and, for each q, the 4 consecutive output
+    // columns 8 q + 4 hb + 0..3 (e = 4 q .. 4 q + 3), one 8-byte LDS write into the tile
+    // [256 tokens][2d columns: K, then V] (rows padded by 8 bytes, so the 32 tokens of a write land
+    // in 32 different bank pairs).  Then every thread copies 16-byte row chunks to K and V.
+    constexpr int OST = 2 * DD * 2 + 8;                   // bytes per token row of the output tile
+    static_assert(kBrM * OST <= NSH * G::HBYTES + NSW * G::WBYTES, "output tile fits the stage buffers");
+    __syncthreads();                                      // every wave is done with the stages
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        const int c = 32 * NB * wn + 32 * j;                     // wave-uniform block column
-        uint16_t* out = c < DD ? a.k_out : a.v_out;
-        const int oc0 = (c < DD ? c : c - DD) + 4 * hb;
+    for (int j = 0; j < NB; ++j)
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-            const int64_t row = m0 + 32 * MB * wm + 32 * i + n;
-            if (row >= a.T) continue;
-            uint16_t* orow = out + row * a.stride + oc0;
+            char* trow = smem + (32 * MB * wm + 32 * i + n) * OST + (32 * NB * wn + 32 * j + 4 * hb) * 2;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const uint32_t lo = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * q]) |
                                     ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 1]) << 16);
                 const uint32_t hi = (uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 2]) |
                                     ((uint32_t)f32_to_bf16_rne(acc[i][j][4 * q + 3]) << 16);
-                if (st8) {
-                    *(u32x2_t*)(orow + 8 * q) = u32x2_t{lo, hi};
-                } else {
-                    orow[8 * q] = (uint16_t)lo; orow[8 * q + 1] = (uint16_t)(lo >> 16);
-                    orow[8 * q + 2] = (uint16_t)hi; orow[8 * q + 3] = (uint16_t)(hi >> 16);
-                }
+                *(u32x2_t*)(trow + 16 * q) = u32x2_t{lo, hi};
             }
+        }
+    __syncthreads();
+    // 16-byte chunks: 2d / 8 per token row (K's d / 8 first); rows past T are skipped
+    constexpr int CPR = 2 * DD / 8;
+    const bool st16 = (a.stride & 7) == 0 && ((uintptr_t)a.k_out & 15) == 0 && ((uintptr_t)a.v_out & 15) == 0;
+    for (int x = tid; x < kBrM * CPR; x += kBrThreads) {
+        const int r = x / CPR, c = x % CPR;
+        const int64_t row = m0 + r;
+        if (row >= a.T) continue;
+        const u32x4_t v = *(const u32x4_t*)(smem + r * OST + 16 * c);
+        uint16_t* dst = (c < CPR / 2 ? a.k_out + 8 * c : a.v_out + 8 * (c - CPR / 2)) + row * a.stride;
+        if (st16) {
+            *(u32x4_t*)dst = v;
+        } else {
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) { dst[2 * w2] = (uint16_t)v[w2]; dst[2 * w2 + 1] = (uint16_t)(v[w2] >> 16); }
         }
     }
 }
